@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the int4 MoE layer on one MI355X (gfx950).
+
+Default workload: the 512-token prefill layer (H=2048, I=512, 256 routed
+experts top-8 + 1 shared, int4 g64 weights with bf16 scale/bias), synthetic
+seeded inputs already resident in HBM. One step = one call of
+moe_prefill_layer: router, top-k, routing metadata, grouped gate/up + SwiGLU,
+grouped down, shared expert and combine. Four copies of the packed weights
+(about 1.8 GB) are used in rotation so the weights stream from HBM rather
+than from the 256 MB Infinity Cache.
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value         tokens/s of the whole layer
+  roofline      the dominant kernel (gate/up GEMM): algorithmic bytes or
+                flops per launch / its mean duration from HIP events recorded
+                on the library's stream around every launch in the timed region
+  cpu_baseline  the CPU oracle timed on this host on the same 512 tokens
+  secondary     the 2048-token Zipf-skewed prefill (bf16 MFMA fraction) and
+                batch-1 decode (HBM GB/s of the GEMV kernels), same method
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer prefill tokens/s at T=512/2048 + % bf16 MFMA peak; decode HBM GB/s"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2516.6
+PREFILL_KERNELS = ["router", "topk", "scan_scatter", "gemm_gateup", "gemm_down_routed",
+                   "gemm_down_shared_combine"]
+DECODE_KERNELS = ["decode_router", "decode_gateup", "decode_down", "decode_combine"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def expert_bytes(H, I):
+    """Stored bytes of one expert's gate+up and down (codes + bf16 scale + bias)."""
+    mat = H * I // 2 + 2 * 2 * H * I // 64
+    return 2 * mat, mat
+
+
+def prefill_setup(name, copies, seed=0):
+    import torch
+    from int4_grouped_gemm_router_amd import binding as B
+    from int4_grouped_gemm_router_amd import synth
+    wl, w, x = synth.generate(name, seed=seed)
+    dw = B.DeviceWeights.from_logical(w)
+    dws = [dw] + [dw.clone() for _ in range(copies - 1)]
+    xd = torch.from_numpy(x).cuda()
+    return wl, w, x, xd, dws
+
+
+def run_prefill(name, steps, warmup, copies):
+    import torch
+    from int4_grouped_gemm_router_amd import binding as B
+    wl, w, x, xd, dws = prefill_setup(name, copies)
+    d = dws[0].dims
+    T, H, I = wl.T, wl.H, wl.I
+    chunk = wl.chunk
+    Tc = chunk if chunk else T
+    chunks = -(-T // Tc)
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ws = B.workspace(d, Tc, B.MODE_PREFILL)
+    ro = B.RouteBuffers(d, T if chunks == 1 else Tc)
+    # routing of this fixed input (for the algorithmic byte count)
+    B.moe_prefill_layer(d, dws[0], xd, y, T, chunk, None, ro, ws)
+    torch.cuda.synchronize()
+    hist = ro.hist.cpu().numpy()
+    for i in range(warmup):
+        B.moe_prefill_layer(d, dws[i % copies], xd, y, T, chunk, None, None, ws)
+    n_ev = 6 * chunks + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+    arrays = [B._event_array(ev) for ev in events]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        B.moe_prefill_layer_profiled(d, dws[i % copies], xd, y, T, chunk, arrays[i], ws=ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.zeros((steps, 6 * chunks))
+    for i in range(steps):
+        for j in range(6 * chunks):
+            per[i, j] = events[i][j].elapsed_time(events[i][j + 1])  # ms
+    kern_ms = per.reshape(steps, chunks, 6).sum(axis=1).mean(axis=0) / chunks  # per launch
+    ms_step = wall * 1e3 / steps
+    U = int((hist > 0).sum()) if chunks == 1 else None
+    gu_b, dn_b = expert_bytes(H, I)
+    gate_up_flops = 2.0 * (wl.k + 1) * Tc * H * 2 * I
+    expert_flops = T * (wl.k + 1) * 6.0 * H * I
+    res = dict(workload=name, T=T, chunk=chunk, ms_per_step=ms_step, tokens_per_s=T / (ms_step / 1e3),
+               kernels_us={k: float(v * 1e3) for k, v in zip(PREFILL_KERNELS, kern_ms)},
+               expert_tflops=expert_flops / (ms_step / 1e3) / 1e12)
+    res["mfma_frac_layer"] = res["expert_tflops"] / PEAK_BF16_TFLOPS
+    gu_ms = float(kern_ms[3])
+    res["gateup_tflops"] = gate_up_flops / (gu_ms / 1e3) / 1e12
+    if U is not None:
+        gu_bytes = (U + 1) * gu_b + T * H * 2 + (wl.k + 1) * T * I * 2
+        res["touched_experts"] = U
+        res["gateup_algorithmic_bytes"] = gu_bytes
+        res["gateup_gbs"] = gu_bytes / (gu_ms / 1e3) / 1e9
+    return res, (w, x)
+
+
+def run_decode(name, steps, warmup, copies):
+    import torch
+    from int4_grouped_gemm_router_amd import binding as B
+    from int4_grouped_gemm_router_amd import synth
+    wl, w, xs = synth.generate(name, steps=steps + warmup)
+    dw = B.DeviceWeights.from_logical(w)
+    dws = [dw] + [dw.clone() for _ in range(copies - 1)]
+    d = dw.dims
+    T, H, I = wl.T, wl.H, wl.I
+    xd = torch.from_numpy(xs).cuda()
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ws = B.workspace(d, T, B.MODE_DECODE)
+    ro = B.RouteBuffers(d, T)
+    for i in range(warmup):
+        B.moe_decode_layer(d, dws[i % copies], xd[i], y, T, None, None, ws)
+    # unique experts per step (for the byte count), from an untimed pass over the same inputs
+    hists = []
+    for i in range(min(steps, 64)):
+        B.moe_decode_layer(d, dws[0], xd[warmup + i], y, T, None, ro, ws)
+        hists.append(ro.hist.clone())
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    arrays = [B._event_array(ev) for ev in events]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        B.moe_decode_layer_profiled(d, dws[i % copies], xd[warmup + i], y, T, arrays[i], ws=ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(4)]
+                    for i in range(steps)])
+    kern_ms = per.mean(axis=0)
+    U = float(np.mean([(h.cpu().numpy() > 0).sum() for h in hists]))
+    gu_b, dn_b = expert_bytes(H, I)
+    gemv_bytes = (U + 1) * (gu_b + dn_b)
+    router_bytes = wl.E * H * 4
+    gemv_ms = float(kern_ms[1] + kern_ms[2])
+    ms_step = wall * 1e3 / steps
+    return dict(workload=name, T=T, steps=steps, ms_per_step=ms_step,
+                unique_experts=U, kernels_us={k: float(v * 1e3) for k, v in zip(DECODE_KERNELS, kern_ms)},
+                gemv_bytes=gemv_bytes, gemv_gbs=gemv_bytes / (gemv_ms / 1e3) / 1e9,
+                step_bytes=gemv_bytes + router_bytes,
+                end_to_end_gbs=(gemv_bytes + router_bytes) / (ms_step / 1e3) / 1e9)
+
+
+def cpu_baseline(w, x, tokens):
+    import oracle
+    sample = np.arange(min(tokens, x.shape[0]))
+    t0 = time.perf_counter()
+    oracle.layer(x, w, tokens=sample)
+    dt = time.perf_counter() - t0
+    return {"value": len(sample) / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "sample": f"first {len(sample)} of the {x.shape[0]} tokens of the "
+            f"same workload, whole layer (router, top-8, 8 routed + shared SwiGLU experts), "
+            f"{dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill_t512")
+    ap.add_argument("--copies", type=int, default=4, help="weight copies rotated (cache guard)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from int4_grouped_gemm_router_amd import binding as B
+    if not os.path.exists(B.LIB_PATH):
+        from int4_grouped_gemm_router_amd import build as Bd
+        Bd.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log(f"device: {torch.cuda.get_device_name(0)}")
+
+    res, (w, x) = run_prefill(args.workload, args.steps, args.warmup, args.copies)
+    log(f"{args.workload}: {res}")
+    gu_us = res["kernels_us"]["gemm_gateup"]
+    dominant = max(res["kernels_us"], key=res["kernels_us"].get)
+    # bound of the gate/up kernel from its arithmetic intensity vs the ridge point
+    gu_flops = 2.0 * (8 + 1) * res["T"] * w.H * 2 * w.I
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if "gateup_algorithmic_bytes" in res and gu_flops / res["gateup_algorithmic_bytes"] < ridge:
+        roofline = {"bound": "hbm", "achieved": res["gateup_gbs"], "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": res["gateup_gbs"] / PEAK_HBM_GBS, "traffic": None,
+                    "kernel": "gemm_gateup", "per_launch_bytes": res["gateup_algorithmic_bytes"],
+                    "mean_us": gu_us}
+    else:
+        roofline = {"bound": "mfma", "achieved": res["gateup_tflops"], "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": res["gateup_tflops"] / PEAK_BF16_TFLOPS,
+                    "traffic": None, "kernel": "gemm_gateup", "mean_us": gu_us}
+    roofline["dominant_kernel"] = dominant
+    out = {
+        "metric": METRIC, "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "T": res["T"], "H": w.H, "I": w.I, "E": w.E,
+                   "top_k": 8, "shared_experts": 1,
+                   "weights": "int4 affine, groups of 64, bf16 scale+bias",
+                   "weight_copies": args.copies, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels_us": res["kernels_us"],
+        "expert_tflops": res["expert_tflops"],
+        "mfma_frac_layer": res["mfma_frac_layer"],
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x, res["T"])
+        log(f"cpu baseline: {out['cpu_baseline']}")
+    if not args.no_secondary:
+        sec = []
+        r2, _ = run_prefill("skew_t2048", max(10, args.steps // 2), args.warmup, args.copies)
+        log(f"skew_t2048: {r2}")
+        sec.append(r2)
+        r3 = run_decode("decode_t1", args.decode_steps, 20, 32)
+        log(f"decode_t1: {r3}")
+        sec.append(r3)
+        out["secondary"] = sec
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,464 @@
+// C ABI of the int4 MoE library: argument checks, workspace carve-up, the
+// chunk loop, and the launches on the caller's stream (include/moe_int4.h).
+#include <algorithm>
+
+#include "../../include/moe_int4.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+bool dims_ok(const moe_dims* d) {
+  return d && d->E > 0 && d->E <= 256 && d->E % 64 == 0 && d->top_k == 8 && d->block_m == 32 &&
+         d->H > 0 && d->H % 256 == 0 && d->H <= 8192 && d->I > 0 && d->I % 128 == 0 &&
+         d->I <= 4096;
+}
+
+int64_t max_blocks(const moe_dims* d, int T) {
+  return ((int64_t)d->top_k * T + d->block_m - 1) / d->block_m + d->E;
+}
+
+int max_items(const moe_dims* d, int T) {
+  return (int)(((int64_t)d->top_k * T + kItemRows - 1) / kItemRows + d->E);
+}
+
+int n_chunks(const moe_dims* d, int T) {
+  return (int)(((int64_t)d->top_k * T + kChunkPairs - 1) / kChunkPairs);
+}
+
+// Split the router's K dimension so that the grid has about 256 blocks.
+int router_splits(const moe_dims* d, int T) {
+  const int tiles = ((T + 63) / 64) * (d->E / 64);
+  const int G = d->H / kGroup;
+  int s = 1;
+  while (s * 2 * tiles <= 256 && s * 2 <= G && G % (s * 2) == 0) s *= 2;
+  return s;
+}
+
+// Bump allocator over the caller's workspace (256-byte aligned pieces).
+struct Carve {
+  uint8_t* base;
+  size_t used = 0;
+  template <class P>
+  P* take(size_t count) {
+    P* p = base ? reinterpret_cast<P*>(base + used) : nullptr;
+    used += (count * sizeof(P) + 255) / 256 * 256;
+    return p;
+  }
+};
+
+struct PrefillWs {
+  float* logit_partial;
+  int32_t *topk_idx, *chunk_hist, *hist, *offsets, *perm, *inv_perm, *block_map, *num_blocks;
+  int32_t *items, *num_items;
+  float* topk_w;
+  uint16_t *xs3, *h, *hs3;
+  float* partial;
+};
+
+PrefillWs carve_prefill(const moe_dims* d, int Tc, void* ws, size_t* bytes) {
+  Carve c{static_cast<uint8_t*>(ws)};
+  PrefillWs w;
+  size_t logit_elems = 0;
+  for (int T = 1; T <= Tc; ++T)
+    logit_elems = std::max(logit_elems, (size_t)router_splits(d, T) * T * d->E);
+  const int k = d->top_k;
+  const int Kx_gu = extra_k(d->H / kGroup), Kx_d = extra_k(d->I / kGroup);
+  w.logit_partial = c.take<float>(logit_elems);
+  w.topk_idx = c.take<int32_t>((size_t)k * Tc);
+  w.topk_w = c.take<float>((size_t)k * Tc);
+  w.chunk_hist = c.take<int32_t>((size_t)n_chunks(d, Tc) * d->E);
+  w.hist = c.take<int32_t>(d->E);
+  w.offsets = c.take<int32_t>(d->E + 1);
+  w.perm = c.take<int32_t>((size_t)k * Tc);
+  w.inv_perm = c.take<int32_t>((size_t)k * Tc);
+  w.block_map = c.take<int32_t>(3 * (size_t)max_blocks(d, Tc));
+  w.num_blocks = c.take<int32_t>(1);
+  w.items = c.take<int32_t>(3 * (size_t)max_items(d, Tc));
+  w.num_items = c.take<int32_t>(1);
+  w.xs3 = c.take<uint16_t>((size_t)Tc * Kx_gu);
+  w.h = c.take<uint16_t>((size_t)(k + 1) * Tc * d->I);
+  w.hs3 = c.take<uint16_t>((size_t)(k + 1) * Tc * Kx_d);
+  w.partial = c.take<float>((size_t)k * Tc * d->H);
+  *bytes = c.used;
+  return w;
+}
+
+struct DecodeWs {
+  float *logits, *topk_w, *partial;
+  int32_t* topk_idx;
+  uint16_t* h;
+};
+
+DecodeWs carve_decode(const moe_dims* d, int T, void* ws, size_t* bytes) {
+  Carve c{static_cast<uint8_t*>(ws)};
+  DecodeWs w;
+  const int k = d->top_k;
+  w.logits = c.take<float>((size_t)T * d->E);
+  w.topk_idx = c.take<int32_t>((size_t)k * T);
+  w.topk_w = c.take<float>((size_t)k * T);
+  w.h = c.take<uint16_t>((size_t)(k + 1) * T * d->I);
+  w.partial = c.take<float>((size_t)(k + 1) * T * d->H);
+  *bytes = c.used;
+  return w;
+}
+
+size_t route_ws(const moe_dims* d, int T, void* ws, int32_t** chunk_hist) {
+  Carve c{static_cast<uint8_t*>(ws)};
+  *chunk_hist = c.take<int32_t>((size_t)n_chunks(d, T) * d->E);
+  return c.used;
+}
+
+bool route_out_ok(const moe_route_out* o) {
+  return o && o->topk_idx && o->topk_w && o->hist && o->offsets && o->perm && o->inv_perm &&
+         o->block_map && o->num_blocks;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+// Optional timing hook: records events[i] before the i-th kernel launch and
+// one more after the last launch.
+struct Recorder {
+  hipEvent_t* ev = nullptr;
+  int n = 0, used = 0;
+  hipError_t mark(hipStream_t s) {
+    if (!ev) return hipSuccess;
+    if (used >= n) return hipErrorInvalidValue;
+    return hipEventRecord(ev[used++], s);
+  }
+};
+
+constexpr int kPrefillLaunchesPerChunk = 6;
+constexpr int kDecodeLaunches = 4;
+
+int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x, uint16_t* y,
+                 int32_t T, int32_t chunk_T, float* logits_out, const moe_route_out* route_out,
+                 void* ws, size_t ws_bytes, void* stream, Recorder rec);
+int decode_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x, uint16_t* y,
+                int32_t T, float* logits_out, const moe_route_out* route_out, void* ws,
+                size_t ws_bytes, void* stream, hipEvent_t* ev);
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_max_blocks(const moe_dims* dims, int32_t T) {
+  if (!dims_ok(dims)) return MOE_EUNSUPPORTED;
+  if (T < 0) return MOE_EINVAL;
+  return max_blocks(dims, T);
+}
+
+int moe_workspace_bytes(const moe_dims* dims, int32_t T_chunk, int32_t mode, size_t* bytes) {
+  if (!bytes || T_chunk < 0) return MOE_EINVAL;
+  if (!dims_ok(dims)) return MOE_EUNSUPPORTED;
+  const int T = std::max(T_chunk, 1);
+  if (mode == 0) {
+    carve_prefill(dims, T, nullptr, bytes);
+  } else if (mode == 1) {
+    if (T > kDecodeMaxT) return MOE_EUNSUPPORTED;
+    carve_decode(dims, T, nullptr, bytes);
+  } else if (mode == 2) {
+    int32_t* ch;
+    *bytes = route_ws(dims, T, nullptr, &ch);
+  } else {
+    return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
+int moe_route(const moe_dims* dims, const float* logits, int32_t T, const moe_route_out* out,
+              void* ws, size_t ws_bytes, void* stream) {
+  if (!dims || T < 0) return MOE_EINVAL;
+  if (!dims_ok(dims)) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!logits || !route_out_ok(out) || !ws) return MOE_EINVAL;
+  int32_t* chunk_hist;
+  if (ws_bytes < route_ws(dims, T, nullptr, &chunk_hist)) return MOE_EWORKSPACE;
+  route_ws(dims, T, ws, &chunk_hist);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_fill_zero(chunk_hist, n_chunks(dims, T) * dims->E, s) != hipSuccess) return MOE_EHIP;
+  TopkArgs ta{};
+  ta.partial = logits;
+  ta.splits = 1;
+  ta.topk_idx = out->topk_idx;
+  ta.topk_w = out->topk_w;
+  ta.chunk_hist = chunk_hist;
+  ta.T = T;
+  ta.E = dims->E;
+  ta.k = dims->top_k;
+  ta.H = dims->H;
+  if (launch_topk(ta, s) != hipSuccess) return MOE_EHIP;
+  ScatterArgs sa{};
+  sa.topk_idx = out->topk_idx;
+  sa.chunk_hist = chunk_hist;
+  sa.hist = out->hist;
+  sa.offsets = out->offsets;
+  sa.perm = out->perm;
+  sa.inv_perm = out->inv_perm;
+  sa.block_map = out->block_map;
+  sa.num_blocks = out->num_blocks;
+  sa.T = T;
+  sa.E = dims->E;
+  sa.k = dims->top_k;
+  sa.block_m = dims->block_m;
+  return hip_status(launch_scan_scatter(sa, s));
+}
+
+int moe_prefill_layer(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x,
+                      uint16_t* y, int32_t T, int32_t chunk_T, float* logits_out,
+                      const moe_route_out* route_out, void* ws, size_t ws_bytes, void* stream) {
+  return prefill_impl(dims, w, x, y, T, chunk_T, logits_out, route_out, ws, ws_bytes, stream,
+                      Recorder{});
+}
+
+int moe_prefill_layer_profiled(const moe_dims* dims, const moe_layer_weights* w,
+                               const uint16_t* x, uint16_t* y, int32_t T, int32_t chunk_T,
+                               float* logits_out, const moe_route_out* route_out, void* ws,
+                               size_t ws_bytes, void* stream, void* const* events,
+                               int32_t n_events) {
+  if (!events || n_events < 0 || !dims || T < 0) return MOE_EINVAL;
+  if (T > 0) {
+    const int Tc = (chunk_T <= 0 || chunk_T > T) ? T : chunk_T;
+    const int chunks = (T + Tc - 1) / Tc;
+    if (n_events < kPrefillLaunchesPerChunk * chunks + 1) return MOE_EINVAL;
+  }
+  Recorder r;
+  r.ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(events));
+  r.n = n_events;
+  return prefill_impl(dims, w, x, y, T, chunk_T, logits_out, route_out, ws, ws_bytes, stream, r);
+}
+
+}  // extern "C"
+
+namespace {
+
+int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x, uint16_t* y,
+                 int32_t T, int32_t chunk_T, float* logits_out, const moe_route_out* route_out,
+                 void* ws, size_t ws_bytes, void* stream, Recorder rec) {
+  if (!dims || T < 0) return MOE_EINVAL;
+  if (!dims_ok(dims)) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!w || !x || !y || !ws || !w->router_w3 || !w->experts_gate_up || !w->experts_down ||
+      !w->shared_gate_up || !w->shared_down)
+    return MOE_EINVAL;
+  if (route_out && !route_out_ok(route_out)) return MOE_EINVAL;
+  const int Tc = (chunk_T <= 0 || chunk_T > T) ? T : chunk_T;
+  size_t need;
+  carve_prefill(dims, Tc, nullptr, &need);
+  if (ws_bytes < need) return MOE_EWORKSPACE;
+  const PrefillWs W = carve_prefill(dims, Tc, ws, &need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = dims->H, I = dims->I, E = dims->E, k = dims->top_k;
+  const int Kx_gu = extra_k(H / kGroup), Kx_d = extra_k(I / kGroup);
+  const PackGeom gu = pack_geom(I, H, 1), dn = pack_geom(H, I, 0);
+  const uint8_t* planes = static_cast<const uint8_t*>(w->router_w3) + kHeaderBytes;
+
+  for (int t0 = 0; t0 < T; t0 += Tc) {
+    const int Tn = std::min(Tc, T - t0);
+    const bool last = t0 + Tc >= T;
+    const moe_route_out* ro = (last && route_out) ? route_out : nullptr;
+    int32_t* topk_idx = ro ? ro->topk_idx : W.topk_idx;
+    float* topk_w = ro ? ro->topk_w : W.topk_w;
+    const uint16_t* xc = x + (int64_t)t0 * H;
+    const int splits = router_splits(dims, Tn);
+    const int nch = n_chunks(dims, Tn);
+
+    if (rec.mark(s) != hipSuccess) return MOE_EHIP;
+    if (launch_router(xc, reinterpret_cast<const uint16_t*>(planes), W.logit_partial, Tn, H, E,
+                      splits, W.chunk_hist, nch * E, s) != hipSuccess)
+      return MOE_EHIP;
+    TopkArgs ta{};
+    ta.partial = W.logit_partial;
+    ta.splits = splits;
+    ta.rbias = w->router_bias;
+    ta.logits_out = logits_out ? logits_out + (int64_t)t0 * E : nullptr;
+    ta.topk_idx = topk_idx;
+    ta.topk_w = topk_w;
+    ta.chunk_hist = W.chunk_hist;
+    ta.x = xc;
+    ta.xs3 = W.xs3;
+    ta.T = Tn;
+    ta.E = E;
+    ta.k = k;
+    ta.H = H;
+    ta.Kx = Kx_gu;
+    if (rec.mark(s) != hipSuccess) return MOE_EHIP;
+    if (launch_topk(ta, s) != hipSuccess) return MOE_EHIP;
+
+    ScatterArgs sa{};
+    sa.topk_idx = topk_idx;
+    sa.chunk_hist = W.chunk_hist;
+    sa.hist = ro ? ro->hist : W.hist;
+    sa.offsets = ro ? ro->offsets : W.offsets;
+    sa.perm = ro ? ro->perm : W.perm;
+    sa.inv_perm = ro ? ro->inv_perm : W.inv_perm;
+    sa.block_map = ro ? ro->block_map : W.block_map;
+    sa.num_blocks = ro ? ro->num_blocks : W.num_blocks;
+    sa.items = W.items;
+    sa.num_items = W.num_items;
+    sa.T = Tn;
+    sa.E = E;
+    sa.k = k;
+    sa.block_m = dims->block_m;
+    if (rec.mark(s) != hipSuccess) return MOE_EHIP;
+    if (launch_scan_scatter(sa, s) != hipSuccess) return MOE_EHIP;
+
+    GemmArgs g{};
+    g.items = W.items;
+    g.num_items = W.num_items;
+    g.T = Tn;
+    g.k = k;
+    g.perm = sa.perm;
+    g.topk_w = topk_w;
+    const int routed = max_items(dims, Tn), shared = (Tn + kItemRows - 1) / kItemRows;
+
+    // gate/up + SwiGLU (routed and shared items in one launch)
+    g.routed_slots = routed;
+    g.shared_slots = shared;
+    g.total_slots = round_up(routed + shared, 8);
+    g.n_tiles = gu.n_wt / 4;
+    g.blob = static_cast<const uint8_t*>(w->experts_gate_up) + kHeaderBytes;
+    g.shared_blob = static_cast<const uint8_t*>(w->shared_gate_up) + kHeaderBytes;
+    g.expert_bytes = gu.expert_bytes;
+    g.N = I;
+    g.K = H;
+    g.paired = 1;
+    g.act = xc;
+    g.act3 = W.xs3;
+    g.Kx = Kx_gu;
+    g.h_out = W.h;
+    g.hs3_out = W.hs3;
+    g.Kx_down = Kx_d;
+    if (rec.mark(s) != hipSuccess) return MOE_EHIP;
+    if (launch_gemm(kGateUp, g, s) != hipSuccess) return MOE_EHIP;
+
+    // routed down, weighted per pair
+    g.routed_slots = routed;
+    g.shared_slots = 0;
+    g.total_slots = round_up(routed, 8);
+    g.n_tiles = dn.n_wt / 4;
+    g.blob = static_cast<const uint8_t*>(w->experts_down) + kHeaderBytes;
+    g.shared_blob = static_cast<const uint8_t*>(w->shared_down) + kHeaderBytes;
+    g.expert_bytes = dn.expert_bytes;
+    g.N = H;
+    g.K = I;
+    g.paired = 0;
+    g.act = W.h;
+    g.act3 = W.hs3;
+    g.Kx = Kx_d;
+    g.partial = W.partial;
+    if (rec.mark(s) != hipSuccess) return MOE_EHIP;
+    if (launch_gemm(kDownRouted, g, s) != hipSuccess) return MOE_EHIP;
+
+    // shared down + combine into y
+    g.routed_slots = 0;
+    g.shared_slots = shared;
+    g.total_slots = round_up(shared, 8);
+    g.y = y + (int64_t)t0 * H;
+    if (rec.mark(s) != hipSuccess) return MOE_EHIP;
+    if (launch_gemm(kDownShared, g, s) != hipSuccess) return MOE_EHIP;
+  }
+  if (rec.mark(s) != hipSuccess) return MOE_EHIP;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_decode_layer(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x,
+                     uint16_t* y, int32_t T, float* logits_out, const moe_route_out* route_out,
+                     void* ws, size_t ws_bytes, void* stream) {
+  return decode_impl(dims, w, x, y, T, logits_out, route_out, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_decode_layer_profiled(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x,
+                              uint16_t* y, int32_t T, float* logits_out,
+                              const moe_route_out* route_out, void* ws, size_t ws_bytes,
+                              void* stream, void* const* events, int32_t n_events) {
+  if (!events || n_events < kDecodeLaunches + 1) return MOE_EINVAL;
+  return decode_impl(dims, w, x, y, T, logits_out, route_out, ws, ws_bytes, stream,
+                     reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)));
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x, uint16_t* y,
+                int32_t T, float* logits_out, const moe_route_out* route_out, void* ws,
+                size_t ws_bytes, void* stream, hipEvent_t* ev) {
+  if (!dims || T < 0) return MOE_EINVAL;
+  if (!dims_ok(dims) || T > kDecodeMaxT) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!w || !x || !y || !ws || !w->router_w || !w->experts_gate_up || !w->experts_down ||
+      !w->shared_gate_up || !w->shared_down)
+    return MOE_EINVAL;
+  if (route_out && !route_out_ok(route_out)) return MOE_EINVAL;
+  size_t need;
+  carve_decode(dims, T, nullptr, &need);
+  if (ws_bytes < need) return MOE_EWORKSPACE;
+  const DecodeWs W = carve_decode(dims, T, ws, &need);
+  const PackGeom gu = pack_geom(dims->I, dims->H, 1), dn = pack_geom(dims->H, dims->I, 0);
+  DecodeArgs a{};
+  a.x = x;
+  a.router_w = w->router_w;
+  a.rbias = w->router_bias;
+  a.logits = W.logits;
+  a.logits_out = logits_out;
+  a.topk_idx = route_out ? route_out->topk_idx : W.topk_idx;
+  a.topk_w = route_out ? route_out->topk_w : W.topk_w;
+  if (route_out) {
+    a.hist = route_out->hist;
+    a.offsets = route_out->offsets;
+    a.perm = route_out->perm;
+    a.inv_perm = route_out->inv_perm;
+    a.block_map = route_out->block_map;
+    a.num_blocks = route_out->num_blocks;
+  }
+  a.gu_blob = static_cast<const uint8_t*>(w->experts_gate_up) + kHeaderBytes;
+  a.gu_shared = static_cast<const uint8_t*>(w->shared_gate_up) + kHeaderBytes;
+  a.gu_expert_bytes = gu.expert_bytes;
+  a.dn_blob = static_cast<const uint8_t*>(w->experts_down) + kHeaderBytes;
+  a.dn_shared = static_cast<const uint8_t*>(w->shared_down) + kHeaderBytes;
+  a.dn_expert_bytes = dn.expert_bytes;
+  a.h = W.h;
+  a.partial = W.partial;
+  a.y = y;
+  a.T = T;
+  a.H = dims->H;
+  a.I = dims->I;
+  a.E = dims->E;
+  a.k = dims->top_k;
+  a.block_m = dims->block_m;
+  return hip_status(launch_decode(a, static_cast<hipStream_t>(stream), ev));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null pointer, negative size or bad mode)";
+    case MOE_EUNSUPPORTED: return "unsupported dimensions";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP launch error";
+    case MOE_EBUFFER: return "output buffer too small";
+    case MOE_EFORMAT: return "int4 code outside 0..15";
+    default: return "unknown error";
+  }
+}
+
+int moe_test_dequant(const void* blob, int32_t count, int32_t N, int32_t K, int32_t paired,
+                     int32_t expert, float* out, void* stream) {
+  if (!blob || !out || expert < 0 || expert >= count) return MOE_EINVAL;
+  if (moe_packed_bytes(count, N, K, paired) == 0) return MOE_EUNSUPPORTED;
+  const PackGeom g = pack_geom(N, K, paired);
+  const uint8_t* base = static_cast<const uint8_t*>(blob) + kHeaderBytes + (int64_t)expert * g.expert_bytes;
+  return hip_status(launch_test_dequant(base, N, K, paired, out, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

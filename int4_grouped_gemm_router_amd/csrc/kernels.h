@@ -1,0 +1,103 @@
+// Internal kernel interfaces of the int4 MoE library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "device.h"
+#include "layout.h"
+
+namespace moe {
+
+constexpr int kChunkPairs = 1024;  // (token, slot) pairs per scatter block
+constexpr int kItemRows = 64;      // rows of one expert per GEMM work item
+constexpr int kMaxGroups = 128;    // H / 64 upper bound
+constexpr int kDecodeMaxT = 4;
+
+struct TopkArgs {
+  const float* partial;   // [splits][T][E]
+  int splits;
+  const float* rbias;     // [E] or null
+  float* logits_out;      // [T][E] or null
+  int32_t* topk_idx;      // [T][k]
+  float* topk_w;          // [T][k]
+  int32_t* chunk_hist;    // [chunks][E] (zeroed beforehand) or null
+  const uint16_t* x;      // [T][H] bf16 (for xs3)
+  uint16_t* xs3;          // [T][Kx] or null
+  int T, E, k, H, Kx;
+};
+
+struct ScatterArgs {
+  const int32_t* topk_idx;
+  const int32_t* chunk_hist;
+  int32_t *hist, *offsets, *perm, *inv_perm, *block_map, *num_blocks;
+  int32_t *items, *num_items;  // GEMM work list or null
+  int T, E, k, block_m;
+};
+
+// Which GEMM: gate/up with SwiGLU, routed down with weighted scatter of the
+// partial outputs, or shared down with the final combine into y.
+enum GemmMode { kGateUp = 0, kDownRouted = 1, kDownShared = 2 };
+
+struct GemmArgs {
+  const int32_t* items;      // routed work list [max][3] (expert, first row, rows)
+  const int32_t* num_items;  // device scalar
+  int routed_slots;          // grid slots reserved for routed items
+  int shared_slots;          // grid slots for shared items (kItemRows tokens each)
+  int total_slots;           // routed + shared, rounded up to a multiple of 8
+  int n_tiles;               // 256-column tiles per item (4 waves x 64 columns)
+  const uint8_t* blob;       // routed experts (past the header)
+  const uint8_t* shared_blob;
+  int64_t expert_bytes;
+  int N, K, paired;          // packed geometry of this matrix set
+  int T;                     // tokens in this chunk
+  int k;                     // experts per token
+  // activations
+  const uint16_t* act;       // gate/up: x [T][K]; down: h [(k+1)T][K]
+  const uint16_t* act3;      // gate/up: xs3 [T][Kx]; down: hs3 [(k+1)T][Kx]
+  int Kx;
+  const int32_t* perm;       // [kT]
+  const float* topk_w;       // [kT]
+  // outputs
+  uint16_t* h_out;           // gate/up: h [(k+1)T][N]
+  uint16_t* hs3_out;         // gate/up: hs3 [(k+1)T][Kx_down]
+  int Kx_down;
+  float* partial;            // down: [kT][N] fp32, weighted per pair
+  uint16_t* y;               // shared down: [T][N] bf16
+};
+
+hipError_t launch_router(const uint16_t* x, const uint16_t* planes, float* partial, int T, int H,
+                         int E, int splits, int* zero_buf, int zero_count, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_scan_scatter(const ScatterArgs& a, hipStream_t s);
+hipError_t launch_fill_zero(int* p, int n, hipStream_t s);
+hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t s);
+hipError_t launch_test_dequant(const uint8_t* expert_base, int N, int K, int paired, float* out,
+                               hipStream_t s);
+
+struct DecodeArgs {
+  const uint16_t* x;          // [T][H]
+  const float* router_w;      // [E][H]
+  const float* rbias;         // [E] or null
+  float* logits;              // [T][E]
+  float* logits_out;          // [T][E] or null
+  int32_t* topk_idx;          // [T][k]
+  float* topk_w;              // [T][k]
+  int32_t *hist, *offsets, *perm, *inv_perm, *block_map, *num_blocks;  // optional route_out
+  const uint8_t* gu_blob;     // routed gate/up experts (past header)
+  const uint8_t* gu_shared;
+  int64_t gu_expert_bytes;
+  const uint8_t* dn_blob;
+  const uint8_t* dn_shared;
+  int64_t dn_expert_bytes;
+  uint16_t* h;                // [k*T + T][I] bf16 (slot order: pairs, then shared)
+  float* partial;             // [k*T + T][H] fp32
+  uint16_t* y;                // [T][H]
+  int T, H, I, E, k, block_m;
+};
+
+// ev (optional): five events recorded before each of the four launches and after the last.
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev = nullptr);
+
+}  // namespace moe

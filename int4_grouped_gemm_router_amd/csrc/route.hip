@@ -1,0 +1,305 @@
+// Router and GPU-resident routing for the int4 MoE layer (gfx950).
+//
+// diariobitcoin.com, "Perplexity libera Lily, un motor de IA que supera a
+// MLX-LM en Apple Silicon": section "Qwen3.6 combina tres cargas de trabajo"
+// (a router scores the experts and keeps eight per token) and section "Las
+// optimizaciones en el prefill" (routing histogram, prefix scan, scatter and
+// block map stay on the GPU, with no CPU synchronisation inside the layer).
+//
+// Kernels, all enqueued on one stream with grids sized from host-known upper
+// bounds so that nothing is read back:
+//   router_mfma   logits partials: x (bf16) * Wr (three exact bf16 planes)
+//                 on the matrix cores, fp32 accumulation, split along H
+//   topk          per token: sum of the partials (+ router bias), top-k with
+//                 ties to the lower index, renormalised softmax weights,
+//                 per-64 group sums of x (for the bias term of the expert
+//                 GEMM), and per-chunk expert counts
+//   scan_scatter  per chunk of 1024 pairs: expert offsets (exclusive scan),
+//                 the chunk's base per expert, a stable scatter of the pairs
+//                 (wave ballot peer matching), and, in block 0, the histogram,
+//                 offsets, the 32-row block map and the GEMM work list.
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- router
+
+// Grid: (ceil(T/64), E/64, KS). Block: 256 threads = 4 waves; wave w owns
+// tokens [64*bx + 16w, +16) and all 64 experts of the tile (4 MFMA tiles).
+__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ planes,
+                                                          float* __restrict__ partial, int T,
+                                                          int H, int E, int groups_per_split,
+                                                          int* __restrict__ zero_buf,
+                                                          int zero_count) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, kb = lane >> 4;
+  const int tt = blockIdx.x, et = blockIdx.y, split = blockIdx.z;
+  const int G = H / kGroup, n_et = E / 64;
+  if (zero_buf && tt == 0 && et == 0 && split == 0)
+    for (int i = threadIdx.x; i < zero_count; i += blockDim.x) zero_buf[i] = 0;
+
+  const int row = tt * 64 + wave * 16 + c16;
+  const bool row_ok = row < T;
+  const uint16_t* xr = x + (int64_t)(row_ok ? row : 0) * H;
+  f32x4 acc[4];
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int g0 = split * groups_per_split;
+  for (int g = g0; g < g0 + groups_per_split; ++g) {
+    u32x4 a[2];
+    for (int ks = 0; ks < 2; ++ks) {
+      a[ks] = row_ok ? *reinterpret_cast<const u32x4*>(xr + g * kGroup + 32 * ks + 8 * kb)
+                     : u32x4{0u, 0u, 0u, 0u};
+    }
+    for (int p = 0; p < 3; ++p)
+      for (int ct = 0; ct < 4; ++ct)
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x4 b = *reinterpret_cast<const u32x4*>(
+              planes + router_index(p, et, g, ct, ks, lane, n_et, G));
+          acc[ct] = mfma16(a[ks], b, acc[ct]);
+        }
+  }
+  float* out = partial + (int64_t)split * T * E;
+  for (int ct = 0; ct < 4; ++ct)
+    for (int i = 0; i < 4; ++i) {
+      const int t = tt * 64 + wave * 16 + 4 * kb + i;
+      if (t < T) out[(int64_t)t * E + et * 64 + ct * 16 + c16] = acc[ct][i];
+    }
+}
+
+// ---------------------------------------------------------------- top-k
+
+// Grid: ceil(T/4); one wave per token.
+__global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  __shared__ float xs_s[4][kMaxGroups];
+  if (t >= a.T) return;
+  const int E = a.E, k = a.k, per = E / 64;
+  float l[4];
+  for (int i = 0; i < 4; ++i) {
+    l[i] = -INFINITY;
+    if (i < per) {
+      const int e = lane + 64 * i;
+      float v = 0.f;
+      for (int s = 0; s < a.splits; ++s) v += a.partial[((int64_t)s * a.T + t) * E + e];
+      if (a.rbias) v += a.rbias[e];
+      if (a.logits_out) a.logits_out[(int64_t)t * E + e] = v;
+      l[i] = v == v ? v : -INFINITY;  // a NaN logit never wins; the selection stays valid
+    }
+  }
+  // top-k by repeated wave argmax; (value desc, index asc)
+  uint32_t taken = 0;
+  int sel_e = -1;
+  float sel_l = 0.f, top = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int i = 0; i < per; ++i) {
+      const int e = lane + 64 * i;
+      if (!((taken >> i) & 1u) && (l[i] > bv || (l[i] == bv && e < bi))) {
+        bv = l[i];
+        bi = e;
+      }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (j == 0) top = bv;
+    if (lane == j) {
+      sel_e = bi;
+      sel_l = bv;
+    }
+  }
+  // weights: exp(l_j - l_0) / sum over the k selected
+  const float p = lane < k ? expf(sel_l - top) : 0.f;
+  const float z = wave_sum(p);
+  if (lane < k) {
+    const int64_t pair = (int64_t)t * k + lane;
+    a.topk_idx[pair] = sel_e;
+    a.topk_w[pair] = p / z;
+    if (a.chunk_hist) atomicAdd(&a.chunk_hist[(pair / kChunkPairs) * E + sel_e], 1);
+  }
+  // per-group sums of x for the expert GEMM's bias term
+  if (a.xs3) {
+    const int G = a.H / kGroup, Gp = round_up(G, 8);
+    const uint16_t* xr = a.x + (int64_t)t * a.H;
+    for (int g0 = 0; g0 < G; g0 += 8) {
+      const int g = g0 + (lane >> 3);
+      float s = 0.f;
+      if (g < G) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xr + g * kGroup + 8 * (lane & 7));
+        s = bf16lo(v.x) + bf16hi(v.x) + bf16lo(v.y) + bf16hi(v.y) + bf16lo(v.z) + bf16hi(v.z) +
+            bf16lo(v.w) + bf16hi(v.w);
+      }
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      s += __shfl_xor(s, 4);
+      if ((lane & 7) == 0 && g < G) xs_s[wave][g] = s;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    uint16_t* out = a.xs3 + (int64_t)t * a.Kx;
+    for (int kk = lane; kk < a.Kx; kk += 64) {
+      const int seg = kk / Gp, g = kk % Gp;
+      uint16_t v = 0;
+      if (seg < 3 && g < G) {
+        uint16_t hi, lo;
+        split_hi_lo(xs_s[wave][g], hi, lo);
+        v = seg == 2 ? lo : hi;
+      }
+      out[kk] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- scan + scatter
+
+__device__ inline int block_exclusive_scan(int v, int* scratch /* >= 4 ints */, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(inc, o);
+    if (lane >= o) inc += n;
+  }
+  if (lane == 63) scratch[wave] = inc;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) base += scratch[w];
+    total += scratch[w];
+  }
+  __syncthreads();
+  return base + inc - v;
+}
+
+// Grid: number of 1024-pair chunks. Block: 256 threads (one per expert).
+__global__ __launch_bounds__(256) void scan_scatter_kernel(ScatterArgs a) {
+  __shared__ int off_s[256];
+  __shared__ int wbase[4][256];
+  __shared__ int scratch[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, P = a.T * a.k;
+  const int chunk = blockIdx.x;
+  const int n_chunks = (P + kChunkPairs - 1) / kChunkPairs;
+  // totals and this chunk's base per expert
+  int tot = 0, before = 0;
+  if (tid < E) {
+    for (int c = 0; c < n_chunks; ++c) {
+      const int v = a.chunk_hist[c * E + tid];
+      tot += v;
+      if (c < chunk) before += v;
+    }
+  }
+  int total;
+  const int off = block_exclusive_scan(tid < E ? tot : 0, scratch, total);
+  if (tid < E) off_s[tid] = off;
+  if (chunk == 0) {
+    if (tid < E) {
+      a.hist[tid] = tot;
+      a.offsets[tid] = off;
+    }
+    if (tid == 0) a.offsets[E] = total;
+    // 32-row routing blocks
+    int nb_total;
+    const int nb = tid < E ? (tot + a.block_m - 1) / a.block_m : 0;
+    const int boff = block_exclusive_scan(nb, scratch, nb_total);
+    for (int i = 0; i < nb; ++i) {
+      int* bm = a.block_map + 3 * (int64_t)(boff + i);
+      bm[0] = tid;
+      bm[1] = off + i * a.block_m;
+      bm[2] = min(a.block_m, tot - i * a.block_m);
+    }
+    if (tid == 0) *a.num_blocks = nb_total;
+    // GEMM work items: up to kItemRows rows of one expert
+    if (a.items) {
+      int ni_total;
+      const int ni = tid < E ? (tot + kItemRows - 1) / kItemRows : 0;
+      const int ioff = block_exclusive_scan(ni, scratch, ni_total);
+      for (int i = 0; i < ni; ++i) {
+        int* it = a.items + 3 * (int64_t)(ioff + i);
+        it[0] = tid;
+        it[1] = off + i * kItemRows;
+        it[2] = min(kItemRows, tot - i * kItemRows);
+      }
+      if (tid == 0) *a.num_items = ni_total;
+    }
+  }
+  // wave-level counts of this chunk's pairs: wave w owns 256 consecutive pairs
+  for (int i = tid; i < 4 * 256; i += 256) (&wbase[0][0])[i] = 0;
+  __syncthreads();
+  const int p0 = chunk * kChunkPairs + wave * 256;
+  for (int r = 0; r < 4; ++r) {
+    const int p = p0 + r * 64 + lane;
+    if (p < P) atomicAdd(&wbase[wave][a.topk_idx[p]], 1);
+  }
+  __syncthreads();
+  if (tid < E) {
+    int run = off_s[tid] + before;
+    for (int w = 0; w < 4; ++w) {
+      const int c = wbase[w][tid];
+      wbase[w][tid] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  // stable scatter: rank among equal experts inside each 64-pair round
+  for (int r = 0; r < 4; ++r) {
+    const int p = p0 + r * 64 + lane;
+    if (p < P) {
+      const int e = a.topk_idx[p];
+      const uint64_t peers = match_any((uint32_t)e, 8);
+      const int rank = __popcll(peers & lanemask_lt());
+      const int pos = wbase[wave][e] + rank;
+      a.perm[pos] = p;
+      a.inv_perm[p] = pos;
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      if (rank == 0) wbase[wave][e] += __popcll(peers);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
+}
+
+__global__ void fill_zero_kernel(int* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_router(const uint16_t* x, const uint16_t* planes, float* partial, int T, int H,
+                         int E, int splits, int* zero_buf, int zero_count, hipStream_t s) {
+  const int G = H / kGroup;
+  dim3 grid((T + 63) / 64, E / 64, splits);
+  hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(256), 0, s, x, planes, partial, T, H, E,
+                     G / splits, zero_buf, zero_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_scatter(const ScatterArgs& a, hipStream_t s) {
+  const int P = a.T * a.k;
+  hipLaunchKernelGGL(scan_scatter_kernel, dim3((P + kChunkPairs - 1) / kChunkPairs), dim3(256),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(int* p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

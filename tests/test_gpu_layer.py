@@ -1,0 +1,198 @@
+"""GPU layer parity against the CPU oracle, through the C ABI.
+
+Covers every workload shape: the tiny layer (all tokens, ragged token counts),
+the 512-token prefill (all tokens), the Zipf-skewed 2048-token prefill
+(sampled tokens incl. the heaviest experts' tokens, routing metadata), the
+16384-token prompt in 4096-token chunks (sampled tokens; chunked equals
+unchunked bit for bit), decode at 1 and 4 tokens, plus edge cases (forced
+heavy routing with empty experts, determinism, T = 0).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from int4_grouped_gemm_router_amd import binding as B
+from int4_grouped_gemm_router_amd import synth
+
+from parity import assert_y_close, check_layer, check_route_meta
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+_cache = {}
+
+
+def _layer(name, seed=0):
+    key = (name, seed)
+    if key not in _cache:
+        wl, w, _ = synth.generate(name, seed=seed, with_x=False)
+        _cache.clear()
+        _cache[key] = (wl, w, B.DeviceWeights.from_logical(w))
+    return _cache[key]
+
+
+def _prefill(torch, dw, x, chunk=0, route=True):
+    d = dw.dims
+    T = x.shape[0]
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty((T, d.H), dtype=torch.int16, device="cuda")
+    logits = torch.empty((T, d.E), dtype=torch.float32, device="cuda")
+    Tc = chunk if chunk else T
+    last = T - ((T - 1) // Tc) * Tc
+    ro = B.RouteBuffers(d, last) if route else None
+    ws = B.workspace(d, Tc, B.MODE_PREFILL)
+    B.moe_prefill_layer(d, dw, xd, y, T, chunk, logits, ro, ws)
+    torch.cuda.synchronize()
+    return (y.cpu().numpy().view(np.uint16), logits.cpu().numpy(),
+            ro.to_numpy() if ro is not None else None)
+
+
+def _route_of(meta_gpu, T):
+    return meta_gpu["topk_idx"].reshape(T, 8), meta_gpu["topk_w"].reshape(T, 8)
+
+
+@pytest.mark.parametrize("T", [1, 5, 17, 32, 64, 100])
+def test_prefill_tiny_all_tokens(torch_cuda, T):
+    wl, w, dw = _layer("tiny_t32")
+    x = synth.make_x(np.random.default_rng(T), T, w.H)
+    y, logits, meta = _prefill(torch_cuda, dw, x)
+    idx, wsel = _route_of(meta, T)
+    s = check_layer(x, w, y, logits, idx, wsel)
+    check_route_meta(meta, idx, 256, 8, 32)
+    print(f"tiny T={T}: {s}")
+
+
+def test_prefill_t512_all_tokens(torch_cuda):
+    wl, w, dw = _layer("prefill_t512")
+    _, _, x = synth.generate("prefill_t512", with_x=True)
+    y, logits, meta = _prefill(torch_cuda, dw, x)
+    idx, wsel = _route_of(meta, 512)
+    s = check_layer(x, w, y, logits, idx, wsel)
+    check_route_meta(meta, idx, 256, 8, 32)
+    # with no near-tie the oracle's own metadata must match bit for bit
+    ref_l = oracle.router_logits(x, w.router_w, w.router_bias)
+    ridx, _ = oracle.topk(ref_l, 8)
+    if np.array_equal(ridx, idx):
+        ref = oracle.route_meta(ridx, 256, 32)
+        for f in ("hist", "offsets", "perm", "inv_perm", "block_map"):
+            assert np.array_equal(meta[f], ref[f]), f
+    print(f"T=512: {s}")
+
+
+def test_prefill_skew_t2048_sampled(torch_cuda):
+    wl, w, dw = _layer("skew_t2048")
+    _, _, x = synth.generate("skew_t2048", with_x=True)
+    T = x.shape[0]
+    y, logits, meta = _prefill(torch_cuda, dw, x)
+    idx, wsel = _route_of(meta, T)
+    check_route_meta(meta, idx, 256, 8, 32)
+    hist = meta["hist"]
+    assert (hist == 0).sum() > 50 and hist.max() > 500, "skewed routing expected"
+    # sample: the first 64 tokens, 64 spread tokens, and 64 tokens of the heaviest expert
+    heavy = int(np.argmax(hist))
+    heavy_tokens = np.nonzero((idx == heavy).any(axis=1))[0]
+    sample = np.unique(np.concatenate([np.arange(64), np.linspace(0, T - 1, 64).astype(int),
+                                       heavy_tokens[:: max(1, len(heavy_tokens) // 64)][:64]]))
+    s = check_layer(x, w, y, logits, idx, wsel, tokens=sample)
+    print(f"skew T=2048 ({len(sample)} sampled): {s}")
+
+
+def test_prefill_long_chunked_sampled(torch_cuda):
+    wl, w, dw = _layer("prefill_t512")   # same layer shape as the long prompt
+    x = synth.make_x(np.random.default_rng(16384), 16384, w.H)
+    y, logits, meta = _prefill(torch_cuda, dw, x, chunk=4096)
+    T = x.shape[0]
+    # the route output holds the last chunk's metadata
+    idx_last, _ = _route_of(meta, 4096)
+    check_route_meta(meta, idx_last, 256, 8, 32)
+    y1, logits1, _ = _prefill(torch_cuda, dw, x, chunk=0, route=False)
+    assert np.array_equal(y, y1), "chunked and unchunked outputs differ"
+    assert np.array_equal(logits, logits1)
+    sample = np.unique(np.concatenate([np.arange(0, T, 128), np.arange(4090, 4100),
+                                       np.arange(T - 16, T)]))
+    # the GPU's selections for every token, from its own logits via moe_route
+    torch = torch_cuda
+    d = dw.dims
+    ro = B.RouteBuffers(d, T)
+    B.moe_route(d, torch.from_numpy(logits).cuda(), T, ro, B.workspace(d, T, B.MODE_ROUTE))
+    torch.cuda.synchronize()
+    idx_all, w_all = _route_of(ro.to_numpy(), T)
+    assert np.array_equal(idx_all[-4096:], idx_last)
+    s = check_layer(x, w, y, logits, idx_all, w_all, tokens=sample)
+    print(f"long T=16384 chunk 4096 ({len(sample)} sampled): {s}")
+
+
+def test_prefill_forced_heavy_routing(torch_cuda):
+    # a router bias that sends nearly every token to experts 0..7 and 100..103:
+    # groups of hundreds of rows, 244 empty experts, ragged 64-row items
+    import copy
+    _, w, _ = _layer("tiny_t32")
+    w2 = copy.deepcopy(w)
+    rb = np.zeros(256, np.float32)
+    rb[:8] = 6.0
+    rb[100:104] = 5.9
+    w2.router_bias = rb
+    dw2 = B.DeviceWeights.from_logical(w2)
+    x = synth.make_x(np.random.default_rng(3), 300, w.H)
+    y, logits, meta = _prefill(torch_cuda, dw2, x)
+    idx, wsel = _route_of(meta, 300)
+    check_route_meta(meta, idx, 256, 8, 32)
+    assert (meta["hist"] == 0).sum() >= 200
+    check_layer(x, w2, y, logits, idx, wsel)
+
+
+def test_prefill_deterministic_and_empty(torch_cuda):
+    _, w, dw = _layer("tiny_t32")
+    x = synth.make_x(np.random.default_rng(9), 77, w.H)
+    y1, l1, m1 = _prefill(torch_cuda, dw, x)
+    y2, l2, m2 = _prefill(torch_cuda, dw, x)
+    assert np.array_equal(y1, y2) and np.array_equal(l1, l2)
+    for f in m1:
+        assert np.array_equal(np.asarray(m1[f]), np.asarray(m2[f])), f
+    # T = 0 enqueues nothing and succeeds
+    B.moe_prefill_layer(dw.dims, dw, None, None, 0)
+
+
+def _decode(torch, dw, x):
+    d = dw.dims
+    T = x.shape[0]
+    y = torch.empty((T, d.H), dtype=torch.int16, device="cuda")
+    logits = torch.empty((T, d.E), dtype=torch.float32, device="cuda")
+    ro = B.RouteBuffers(d, T)
+    ws = B.workspace(d, T, B.MODE_DECODE)
+    B.moe_decode_layer(d, dw, torch.from_numpy(x).cuda(), y, T, logits, ro, ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().view(np.uint16), logits.cpu().numpy(), ro.to_numpy()
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_matches_oracle(torch_cuda, T):
+    wl, w, dw = _layer("prefill_t512")
+    rng = np.random.default_rng(40 + T)
+    for step in range(3):
+        x = synth.make_x(rng, T, w.H)
+        y, logits, meta = _decode(torch_cuda, dw, x)
+        idx, wsel = _route_of(meta, T)
+        s = check_layer(x, w, y, logits, idx, wsel)
+        check_route_meta(meta, idx, 256, 8, 32)
+        uniq = np.unique(idx)
+        assert meta["num_blocks"] == len(uniq)
+        assert np.array_equal(meta["block_map"][:, 0], uniq)
+        print(f"decode T={T} step {step}: {s}")
+
+
+def test_decode_tiny_and_vs_prefill(torch_cuda):
+    _, w, dw = _layer("tiny_t32")
+    x = synth.make_x(np.random.default_rng(11), 4, w.H)
+    yd, ld, md = _decode(torch_cuda, dw, x)
+    yp, lp, mp = _prefill(torch_cuda, dw, x)
+    check_layer(x, w, yd, ld, *_route_of(md, 4))
+    if np.array_equal(md["topk_idx"], mp["topk_idx"]):
+        assert_y_close(synth.bf16_bits_to_f32(yd), synth.bf16_bits_to_f32(yp), "decode vs prefill")
