@@ -14,7 +14,7 @@ import re
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe_int4.so")
+LIB_PATH = os.environ.get("MOE_INT4_LIB", os.path.join(HERE, "libmoe_int4.so"))
 HEADER = os.path.join(os.path.dirname(HERE), "include", "moe_int4.h")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_EBUFFER, MOE_EFORMAT = (

@@ -27,12 +27,13 @@ int n_chunks(const moe_dims* d, int T) {
   return (int)(((int64_t)d->top_k * T + kChunkPairs - 1) / kChunkPairs);
 }
 
-// Split the router's K dimension so that the grid has about 256 blocks.
+// Split the router's K dimension (at most kMaxSplits ways) so that the grid
+// has about 128..256 blocks.
 int router_splits(const moe_dims* d, int T) {
   const int tiles = ((T + 63) / 64) * (d->E / 64);
   const int G = d->H / kGroup;
   int s = 1;
-  while (s * 2 * tiles <= 256 && s * 2 <= G && G % (s * 2) == 0) s *= 2;
+  while (s * 2 <= kMaxSplits && s * 2 * tiles <= 256 && s * 2 <= G && G % (s * 2) == 0) s *= 2;
   return s;
 }
 
@@ -80,7 +81,7 @@ PrefillWs carve_prefill(const moe_dims* d, int Tc, void* ws, size_t* bytes) {
   w.xs3 = c.take<uint16_t>((size_t)Tc * Kx_gu);
   w.h = c.take<uint16_t>((size_t)(k + 1) * Tc * d->I);
   w.hs3 = c.take<uint16_t>((size_t)(k + 1) * Tc * Kx_d);
-  w.partial = c.take<float>((size_t)k * Tc * d->H);
+  w.partial = c.take<float>((size_t)(k + 1) * Tc * d->H);
   *bytes = c.used;
   return w;
 }
@@ -333,10 +334,10 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;
     if (launch_gemm(kGateUp, g, s) != hipSuccess) return MOE_EHIP;
 
-    // routed down, weighted per pair
+    // down: routed items (weighted per pair) and shared items in one launch
     g.routed_slots = routed;
-    g.shared_slots = 0;
-    g.total_slots = round_up(routed, 8);
+    g.shared_slots = shared;
+    g.total_slots = round_up(routed + shared, 8);
     g.n_tiles = dn.n_wt / 4;
     g.blob = static_cast<const uint8_t*>(w->experts_down) + kHeaderBytes;
     g.shared_blob = static_cast<const uint8_t*>(w->shared_down) + kHeaderBytes;
@@ -349,15 +350,12 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
     g.Kx = Kx_d;
     g.partial = W.partial;
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;
-    if (launch_gemm(kDownRouted, g, s) != hipSuccess) return MOE_EHIP;
+    if (launch_gemm(kDown, g, s) != hipSuccess) return MOE_EHIP;
 
-    // shared down + combine into y
-    g.routed_slots = 0;
-    g.shared_slots = shared;
-    g.total_slots = round_up(shared, 8);
-    g.y = y + (int64_t)t0 * H;
+    // y = bf16(shared + sum of the k weighted expert outputs)
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;
-    if (launch_gemm(kDownShared, g, s) != hipSuccess) return MOE_EHIP;
+    if (launch_combine(W.partial, topk_w, y + (int64_t)t0 * H, Tn, H, k, s) != hipSuccess)
+      return MOE_EHIP;
   }
   if (rec.mark(s) != hipSuccess) return MOE_EHIP;
   return MOE_OK;

@@ -15,9 +15,10 @@
 //                   then gate/up + SwiGLU for (unique expert or shared expert)
 //                   x (64-column wave tile); block 0 also writes the routing
 //                   metadata
-//   decode_down     down projection per (expert, 64-row tile), times the
-//                   routing weight, into per-pair fp32 rows
-//   decode_combine  y = bf16(shared + sum over the token's k pairs)
+//   decode_down     down projection per (expert, 64-row tile) into
+//                   per-(token, slot) fp32 rows
+//   combine         y = bf16(shared + sum over the token's k slots), the same
+//                   kernel as the prefill path
 #include "kernels.h"
 
 namespace moe {
@@ -232,9 +233,9 @@ __global__ __launch_bounds__(512) void decode_gateup_kernel(DecodeArgs a) {
   for (int gi = 0; gi < gpw; ++gi) {
     const int g = wave * gpw + gi;
     if (g >= G) break;
-    const uint8_t* nib = ebase + geom.nib_off + (((int64_t)wt * G + g) * 64 + lane) * 32;
+    const uint8_t* nib = ebase + geom.nib_off + (((int64_t)wt * G + g) * 128 + lane) * 16;
     const u32x4 w0 = *reinterpret_cast<const u32x4*>(nib);
-    const u32x4 w1 = *reinterpret_cast<const u32x4*>(nib + 16);
+    const u32x4 w1 = *reinterpret_cast<const u32x4*>(nib + 1024);
     const u32x2 sc = *reinterpret_cast<const u32x2*>(
         ebase + geom.scl_off + (((int64_t)wt * G + g) * 16 + c16) * 8);
     const uint16_t* bia = reinterpret_cast<const uint16_t*>(ebase + geom.bia_off);
@@ -317,9 +318,9 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   for (int gi = 0; gi < gpw; ++gi) {
     const int g = wave * gpw + gi;
     if (g >= G) break;
-    const uint8_t* nib = ebase + geom.nib_off + (((int64_t)wt * G + g) * 64 + lane) * 32;
+    const uint8_t* nib = ebase + geom.nib_off + (((int64_t)wt * G + g) * 128 + lane) * 16;
     const u32x4 w0 = *reinterpret_cast<const u32x4*>(nib);
-    const u32x4 w1 = *reinterpret_cast<const u32x4*>(nib + 16);
+    const u32x4 w1 = *reinterpret_cast<const u32x4*>(nib + 1024);
     const u32x2 sc = *reinterpret_cast<const u32x2*>(
         ebase + geom.scl_off + (((int64_t)wt * G + g) * 16 + c16) * 8);
     const uint16_t* bia = reinterpret_cast<const uint16_t*>(ebase + geom.bia_off);
@@ -358,22 +359,9 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
     if (jslot[t] >= 0) {
       float d = 0.f;
       for (int w = 0; w < kDecWaves; ++w) d += red[w][t][j];
-      const bool shared = jslot[t] == k;
-      const int row = shared ? k * T + t : t * k + jslot[t];
-      const float wv = shared ? 1.f : r.sel_w[t][jslot[t]];
-      a.partial[(int64_t)row * H + 64 * wt + j] = wv * d;
+      a.partial[((int64_t)t * (k + 1) + jslot[t]) * H + 64 * wt + j] = d;
     }
   }
-}
-
-// Grid: ceil(T*H/256); y = bf16(shared + sum_j weighted pair outputs).
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= a.T * a.H) return;
-  const int t = i / a.H, n = i % a.H;
-  float v = a.partial[((int64_t)a.k * a.T + t) * a.H + n];
-  for (int j = 0; j < a.k; ++j) v += a.partial[((int64_t)t * a.k + j) * a.H + n];
-  a.y[i] = f2bf(v);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
@@ -388,7 +376,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return e;
   hipLaunchKernelGGL(decode_down_kernel, dim3(slots * dn.n_wt), dim3(512), 0, s, a);
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((a.T * a.H + 255) / 256), dim3(256), 0, s, a);
+  if ((e = launch_combine(a.partial, a.topk_w, a.y, a.T, a.H, a.k, s)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[4], s)) != hipSuccess) return e;
   return hipGetLastError();
 }

@@ -21,15 +21,31 @@ __device__ inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Constants of the int4 -> bf16 expansion, materialised once per kernel in
+// registers. Hiding their values from the optimiser lets the instruction
+// selector fuse (w & mask) | magic into one v_and_or_b32 (gfx9 VOP3 forms take
+// no literal, so with literal constants it emits a separate AND and OR); the
+// fused op is ordinary compiler output, so the hazard recognizer still sees
+// it when it is interleaved with matrix-core instructions.
+struct ExpandConsts {
+  uint32_t mask, magic;
+};
+
+__device__ inline ExpandConsts expand_consts() {
+  ExpandConsts k;
+  asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(k.mask));
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(k.magic));
+  return k;
+}
+
 // Eight int4 codes (one u32 in the packed order) -> eight exact bf16 values
-// 128 + q, two per 32-bit lane word.
-__device__ inline u32x4 expand_codes(uint32_t w) {
-  const uint32_t m = 0x000F000Fu, magic = 0x43004300u;
+// 128 + q, two per 32-bit lane word: bf16 0x4300 | q is 128 + q exactly.
+__device__ inline u32x4 expand_codes(uint32_t w, ExpandConsts k) {
   u32x4 r;
-  r.x = (w & m) | magic;
-  r.y = ((w >> 4) & m) | magic;
-  r.z = ((w >> 8) & m) | magic;
-  r.w = ((w >> 12) & m) | magic;
+  r.x = (w & k.mask) | k.magic;
+  r.y = ((w >> 4) & k.mask) | k.magic;
+  r.z = ((w >> 8) & k.mask) | k.magic;
+  r.w = ((w >> 12) & k.mask) | k.magic;
   return r;
 }
 
@@ -56,6 +72,8 @@ __device__ inline float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // Barrier for LDS hand-off only: waits for this wave's LDS operations, not
 // for its outstanding global loads (a plain __syncthreads would drain them).
+// The memory clobber keeps the compiler from moving LDS or global memory
+// operations across it.
 __device__ inline void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }

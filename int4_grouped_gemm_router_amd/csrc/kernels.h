@@ -11,9 +11,10 @@
 namespace moe {
 
 constexpr int kChunkPairs = 1024;  // (token, slot) pairs per scatter block
-constexpr int kItemRows = 64;      // rows of one expert per GEMM work item
+constexpr int kItemRows = 32;      // rows of one expert per GEMM work item (one routing block)
 constexpr int kMaxGroups = 128;    // H / 64 upper bound
 constexpr int kDecodeMaxT = 4;
+constexpr int kMaxSplits = 4;      // router K splits summed by the top-k kernel
 
 struct TopkArgs {
   const float* partial;   // [splits][T][E]
@@ -36,9 +37,9 @@ struct ScatterArgs {
   int T, E, k, block_m;
 };
 
-// Which GEMM: gate/up with SwiGLU, routed down with weighted scatter of the
-// partial outputs, or shared down with the final combine into y.
-enum GemmMode { kGateUp = 0, kDownRouted = 1, kDownShared = 2 };
+// Which GEMM: gate/up with SwiGLU, or down (routed and shared items) writing
+// per-(token, slot) fp32 rows that the combine kernel sums into y.
+enum GemmMode { kGateUp = 0, kDown = 1 };
 
 struct GemmArgs {
   const int32_t* items;      // routed work list [max][3] (expert, first row, rows)
@@ -63,8 +64,7 @@ struct GemmArgs {
   uint16_t* h_out;           // gate/up: h [(k+1)T][N]
   uint16_t* hs3_out;         // gate/up: hs3 [(k+1)T][Kx_down]
   int Kx_down;
-  float* partial;            // down: [kT][N] fp32, weighted per pair
-  uint16_t* y;               // shared down: [T][N] bf16
+  float* partial;            // down: [T][k+1][N] fp32; slot j < k routed, slot k shared
 };
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* planes, float* partial, int T, int H,
@@ -73,6 +73,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_scan_scatter(const ScatterArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(int* p, int n, hipStream_t s);
 hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t s);
+// y[t][n] = bf16(partial[t][k][n] + sum_{j<k} topk_w[t][j] * partial[t][j][n]) (fixed order).
+hipError_t launch_combine(const float* partial, const float* topk_w, uint16_t* y, int T, int N,
+                          int k, hipStream_t s);
 hipError_t launch_test_dequant(const uint8_t* expert_base, int N, int K, int paired, float* out,
                                hipStream_t s);
 
@@ -92,7 +95,7 @@ struct DecodeArgs {
   const uint8_t* dn_shared;
   int64_t dn_expert_bytes;
   uint16_t* h;                // [k*T + T][I] bf16 (slot order: pairs, then shared)
-  float* partial;             // [k*T + T][H] fp32
+  float* partial;             // [T][k+1][H] fp32 (slot k: shared expert)
   uint16_t* y;                // [T][H]
   int T, H, I, E, k, block_m;
 };

@@ -10,11 +10,12 @@
 // whatever order the hardware walks K in.
 //
 // Per expert, three regions (byte offsets from the expert base):
-//   nib  [wt][g][lane 64][32 B]  eight u32 words per lane: word 2*ct + ks holds
-//        the codes of column 16*ct + c16 for k = 64g + 32ks + 8kb + o, o = 0..7,
-//        code o at nibble position (o & 1) * 4 + (o >> 1); with that order
-//        ((w >> 4d) & 0x000F000F) | 0x43004300 is the bf16 pair
-//        (128 + q[2d], 128 + q[2d+1]) for d = 0..3.
+//   nib  [wt][g][half 2][lane 64][16 B]  eight u32 words per lane, words
+//        0..3 in half 0 and 4..7 in half 1 (so each half is one contiguous
+//        1 KB wave load): word 2*ct + ks holds the codes of column 16*ct + c16
+//        for k = 64g + 32ks + 8kb + o, o = 0..7, code o at nibble position
+//        (o & 1) * 4 + (o >> 1); with that order ((w >> 4d) & 0x000F000F) |
+//        0x43004300 is the bf16 pair (128 + q[2d], 128 + q[2d+1]), d = 0..3.
 //   scl  [wt][g][c16 16][ct 4]   bf16 scale of column 16*ct + c16, group g.
 //   bia  [wt][col 64][Gp]        bf16 bias, groups contiguous per column, zero
 //                                padded from G to Gp = roundup(G, 8).
@@ -65,6 +66,11 @@ __host__ __device__ inline PackGeom pack_geom(int N, int K, int paired) {
   int64_t end = g.bia_off + (int64_t)g.n_wt * kWaveCols * g.Gp * 2;
   g.expert_bytes = (end + 255) / 256 * 256;
   return g;
+}
+
+// u32 index (from the expert's nib base) of word u (0..7) of `lane`.
+__host__ __device__ inline int64_t nib_word(int wt, int g, int lane, int u, int G) {
+  return ((((int64_t)wt * G + g) * 2 + (u >> 2)) * 64 + lane) * 4 + (u & 3);
 }
 
 // Nibble position of code o (0..7) inside its 32-bit word.

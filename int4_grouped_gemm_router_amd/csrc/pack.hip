@@ -79,7 +79,7 @@ extern "C" int pack_int4_g64(const uint8_t* q0, const uint16_t* s0, const uint16
                 if (code > 15) return MOE_EFORMAT;
                 word |= (uint32_t)code << (4 * nibble_pos(o));
               }
-              nib[(((int64_t)wt * g.G + gi) * 64 + lane) * 8 + 2 * ct + ks] = word;
+              nib[nib_word(wt, gi, lane, 2 * ct + ks, g.G)] = word;
             }
         }
       }

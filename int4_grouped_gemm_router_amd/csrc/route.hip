@@ -44,20 +44,34 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
   const uint16_t* xr = x + (int64_t)(row_ok ? row : 0) * H;
   f32x4 acc[4];
   for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int g0 = split * groups_per_split;
-  for (int g = g0; g < g0 + groups_per_split; ++g) {
-    u32x4 a[2];
-    for (int ks = 0; ks < 2; ++ks) {
-      a[ks] = row_ok ? *reinterpret_cast<const u32x4*>(xr + g * kGroup + 32 * ks + 8 * kb)
-                     : u32x4{0u, 0u, 0u, 0u};
+  const int g0 = split * groups_per_split, g1 = g0 + groups_per_split;
+  // four groups per step; every load of a (plane, column tile) pair is issued
+  // before its matrix-core ops so that many loads are in flight per wave
+  for (int gb = g0; gb < g1; gb += 4) {
+    u32x4 a[4][2];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        a[gi][ks] = (row_ok && gb + gi < g1)
+                        ? *reinterpret_cast<const u32x4*>(xr + (gb + gi) * kGroup + 32 * ks + 8 * kb)
+                        : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int pc = 0; pc < 12; ++pc) {
+      const int p = pc >> 2, ct = pc & 3;
+      u32x4 b[4][2];
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          b[gi][ks] = gb + gi < g1 ? *reinterpret_cast<const u32x4*>(
+                                         planes + router_index(p, et, gb + gi, ct, ks, lane, n_et, G))
+                                   : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) acc[ct] = mfma16(a[gi][ks], b[gi][ks], acc[ct]);
     }
-    for (int p = 0; p < 3; ++p)
-      for (int ct = 0; ct < 4; ++ct)
-        for (int ks = 0; ks < 2; ++ks) {
-          const u32x4 b = *reinterpret_cast<const u32x4*>(
-              planes + router_index(p, et, g, ct, ks, lane, n_et, G));
-          acc[ct] = mfma16(a[ks], b, acc[ct]);
-        }
   }
   float* out = partial + (int64_t)split * T * E;
   for (int ct = 0; ct < 4; ++ct)
@@ -76,13 +90,23 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   __shared__ float xs_s[4][kMaxGroups];
   if (t >= a.T) return;
   const int E = a.E, k = a.k, per = E / 64;
+  // all partial loads first (splits <= kMaxSplits), then a fixed-order sum
+  float pv[kMaxSplits][4];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      pv[sp][i] = (sp < a.splits && i < per) ? a.partial[((int64_t)sp * a.T + t) * E + lane + 64 * i]
+                                             : 0.f;
   float l[4];
+#pragma unroll
   for (int i = 0; i < 4; ++i) {
     l[i] = -INFINITY;
     if (i < per) {
       const int e = lane + 64 * i;
       float v = 0.f;
-      for (int s = 0; s < a.splits; ++s) v += a.partial[((int64_t)s * a.T + t) * E + e];
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplits; ++sp) v += pv[sp][i];
       if (a.rbias) v += a.rbias[e];
       if (a.logits_out) a.logits_out[(int64_t)t * E + e] = v;
       l[i] = v == v ? v : -INFINITY;  // a NaN logit never wins; the selection stays valid
@@ -130,18 +154,24 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   if (a.xs3) {
     const int G = a.H / kGroup, Gp = round_up(G, 8);
     const uint16_t* xr = a.x + (int64_t)t * a.H;
-    for (int g0 = 0; g0 < G; g0 += 8) {
-      const int g = g0 + (lane >> 3);
-      float s = 0.f;
-      if (g < G) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(xr + g * kGroup + 8 * (lane & 7));
-        s = bf16lo(v.x) + bf16hi(v.x) + bf16lo(v.y) + bf16hi(v.y) + bf16lo(v.z) + bf16hi(v.z) +
-            bf16lo(v.w) + bf16hi(v.w);
+    for (int gb = 0; gb < G; gb += 32) {
+      u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int g = gb + 8 * u + (lane >> 3);
+        v[u] = g < G ? *reinterpret_cast<const u32x4*>(xr + g * kGroup + 8 * (lane & 7))
+                     : u32x4{0u, 0u, 0u, 0u};
       }
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      if ((lane & 7) == 0 && g < G) xs_s[wave][g] = s;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int g = gb + 8 * u + (lane >> 3);
+        float s = bf16lo(v[u].x) + bf16hi(v[u].x) + bf16lo(v[u].y) + bf16hi(v[u].y) +
+                  bf16lo(v[u].z) + bf16hi(v[u].z) + bf16lo(v[u].w) + bf16hi(v[u].w);
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 4);
+        if ((lane & 7) == 0 && g < G) xs_s[wave][g] = s;
+      }
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");

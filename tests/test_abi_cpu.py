@@ -28,7 +28,7 @@ def test_library_exports_every_header_symbol():
 
 def _read_packed(blob, count, N, K, paired):
     """Recover (q, scale, bias) per matrix from a blob, following the layout
-    documented in csrc/layout.h: per expert nib [wt][g][lane][8 words],
+    documented in csrc/layout.h: per expert nib [wt][g][half][lane][4 words],
     scl [wt][g][c16][ct], bia [wt][col][Gp]; codes o at nibble (o&1)*4 + o>>1."""
     hdr = np.frombuffer(blob[:32].tobytes(), dtype=np.int32)
     assert hdr[0] == 0x4734494D and hdr[1] == 1
@@ -47,7 +47,8 @@ def _read_packed(blob, count, N, K, paired):
     pos = np.array([(o & 1) * 4 + (o >> 1) for o in range(8)])
     for e in range(count):
         base = 256 + e * ebytes
-        words = np.frombuffer(blob[base:base + nib_bytes].tobytes(), np.uint32).reshape(n_wt, G, 64, 8)
+        words = np.frombuffer(blob[base:base + nib_bytes].tobytes(), np.uint32).reshape(n_wt, G, 2, 64, 4)
+        words = words.transpose(0, 1, 3, 2, 4).reshape(n_wt, G, 64, 8)
         scl = np.frombuffer(blob[base + nib_bytes:base + nib_bytes + scl_bytes].tobytes(),
                             np.uint16).reshape(n_wt, G, 16, 4)
         bia = np.frombuffer(blob[base + nib_bytes + scl_bytes:base + end].tobytes(),
