@@ -26,13 +26,29 @@ namespace moe {
 
 // Grid: (ceil(T/64), E/64, KS). Block: 256 threads = 4 waves; wave w owns
 // tokens [64*bx + 16w, +16) and all 64 experts of the tile (4 MFMA tiles).
+// The three bf16 planes of the 64-expert weight tile (24 KB per 64-input
+// group) are shared by the four waves: they arrive in a three-stage LDS ring
+// by asynchronous global -> LDS copies, six 1 KB copies per wave per group;
+// the activation fragments arrive in a register ring alongside.
+constexpr int kRStages = 3;
+
+__device__ inline void router_wait(int groups) {
+  // eight loads per group per wave: six plane copies and two activation loads
+  if (groups >= 1)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ planes,
                                                           float* __restrict__ partial, int T,
                                                           int H, int E, int groups_per_split,
                                                           int* __restrict__ zero_buf,
                                                           int zero_count) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ u32x4 bt[kRStages][3 * 512];  // [stage][plane][ct 4][ks 2][lane 64]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, kb = lane >> 4;
   const int tt = blockIdx.x, et = blockIdx.y, split = blockIdx.z;
   const int G = H / kGroup, n_et = E / 64;
@@ -41,36 +57,44 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
 
   const int row = tt * 64 + wave * 16 + c16;
   const bool row_ok = row < T;
-  const uint16_t* xr = x + (int64_t)(row_ok ? row : 0) * H;
+  const uint16_t* xr = x + (int64_t)(row_ok ? row : 0) * H + 8 * kb;
+  const uint8_t* pl = reinterpret_cast<const uint8_t*>(planes);
+  const int g0 = split * groups_per_split, ng = groups_per_split;
+  u32x4 aq[kRStages][2];
+  auto issue = [&](int gi, int st) {
+    const int g = g0 + gi;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int q = wave * 6 + i;            // 1 KB chunk of the 24 KB tile
+      const int p = q >> 3, part = q & 7;
+      const uint8_t* src = pl + ((((int64_t)p * n_et + et) * G + g) * 8 + part) * 1024 + lane * 16;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&bt[st][p * 512 + part * 64], 16, 0, 0);
+    }
+    aq[st][0] = *reinterpret_cast<const u32x4*>(xr + g * kGroup);
+    aq[st][1] = *reinterpret_cast<const u32x4*>(xr + g * kGroup + 32);
+  };
   f32x4 acc[4];
   for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int g0 = split * groups_per_split, g1 = g0 + groups_per_split;
-  // four groups per step; every load of a (plane, column tile) pair is issued
-  // before its matrix-core ops so that many loads are in flight per wave
-  for (int gb = g0; gb < g1; gb += 4) {
-    u32x4 a[4][2];
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi)
+  for (int d = 0; d < kRStages - 1; ++d)
+    if (d < ng) issue(d, d);
+  for (int gb = 0; gb < ng; gb += kRStages) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        a[gi][ks] = (row_ok && gb + gi < g1)
-                        ? *reinterpret_cast<const u32x4*>(xr + (gb + gi) * kGroup + 32 * ks + 8 * kb)
-                        : u32x4{0u, 0u, 0u, 0u};
+    for (int d = 0; d < kRStages; ++d) {
+      const int gi = gb + d;
+      if (gi >= ng) break;
+      router_wait(min(kRStages - 2, ng - 1 - gi));
+      lds_barrier();
+      if (gi + kRStages - 1 < ng) issue(gi + kRStages - 1, (d + kRStages - 1) % kRStages);
+      const u32x4 a0 = row_ok ? aq[d][0] : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 a1 = row_ok ? aq[d][1] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int pc = 0; pc < 12; ++pc) {
-      const int p = pc >> 2, ct = pc & 3;
-      u32x4 b[4][2];
+      for (int p = 0; p < 3; ++p)
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          b[gi][ks] = gb + gi < g1 ? *reinterpret_cast<const u32x4*>(
-                                         planes + router_index(p, et, gb + gi, ct, ks, lane, n_et, G))
-                                   : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) acc[ct] = mfma16(a[gi][ks], b[gi][ks], acc[ct]);
+        for (int ct = 0; ct < 4; ++ct) {
+          acc[ct] = mfma16(a0, bt[d][p * 512 + (2 * ct) * 64 + lane], acc[ct]);
+          acc[ct] = mfma16(a1, bt[d][p * 512 + (2 * ct + 1) * 64 + lane], acc[ct]);
+        }
     }
   }
   float* out = partial + (int64_t)split * T * E;
@@ -90,7 +114,9 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   __shared__ float xs_s[4][kMaxGroups];
   if (t >= a.T) return;
   const int E = a.E, k = a.k, per = E / 64;
-  // all partial loads first (splits <= kMaxSplits), then a fixed-order sum
+  // all partial loads first (splits <= kMaxSplits), then a fixed-order sum;
+  // the activation loads for the group sums are issued with them so that
+  // the two round trips overlap
   float pv[kMaxSplits][4];
 #pragma unroll
   for (int sp = 0; sp < kMaxSplits; ++sp)
@@ -98,6 +124,16 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     for (int i = 0; i < 4; ++i)
       pv[sp][i] = (sp < a.splits && i < per) ? a.partial[((int64_t)sp * a.T + t) * E + lane + 64 * i]
                                              : 0.f;
+  constexpr int kXPre = 4;  // group-sum loads issued up front: H <= 2048
+  const int G = a.H / kGroup;
+  const uint16_t* xrow = a.xs3 ? a.x + (int64_t)t * a.H : nullptr;
+  u32x4 xv[kXPre];
+#pragma unroll
+  for (int u = 0; u < kXPre; ++u) {
+    const int g = 8 * u + (lane >> 3);
+    xv[u] = (xrow && g < G) ? *reinterpret_cast<const u32x4*>(xrow + g * kGroup + 8 * (lane & 7))
+                            : u32x4{0u, 0u, 0u, 0u};
+  }
   float l[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -152,25 +188,27 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   }
   // per-group sums of x for the expert GEMM's bias term
   if (a.xs3) {
-    const int G = a.H / kGroup, Gp = round_up(G, 8);
-    const uint16_t* xr = a.x + (int64_t)t * a.H;
-    for (int gb = 0; gb < G; gb += 32) {
-      u32x4 v[4];
+    const int Gp = round_up(G, 8);
+    for (int gb = 0; gb < G; gb += 8 * kXPre) {
+      u32x4 v[kXPre];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kXPre; ++u) {
         const int g = gb + 8 * u + (lane >> 3);
-        v[u] = g < G ? *reinterpret_cast<const u32x4*>(xr + g * kGroup + 8 * (lane & 7))
-                     : u32x4{0u, 0u, 0u, 0u};
+        if (gb == 0)
+          v[u] = xv[u];
+        else
+          v[u] = g < G ? *reinterpret_cast<const u32x4*>(xrow + g * kGroup + 8 * (lane & 7))
+                       : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kXPre; ++u) {
         const int g = gb + 8 * u + (lane >> 3);
-        float s = bf16lo(v[u].x) + bf16hi(v[u].x) + bf16lo(v[u].y) + bf16hi(v[u].y) +
-                  bf16lo(v[u].z) + bf16hi(v[u].z) + bf16lo(v[u].w) + bf16hi(v[u].w);
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        if ((lane & 7) == 0 && g < G) xs_s[wave][g] = s;
+        float sum = bf16lo(v[u].x) + bf16hi(v[u].x) + bf16lo(v[u].y) + bf16hi(v[u].y) +
+                    bf16lo(v[u].z) + bf16hi(v[u].z) + bf16lo(v[u].w) + bf16hi(v[u].w);
+        sum += __shfl_xor(sum, 1);
+        sum += __shfl_xor(sum, 2);
+        sum += __shfl_xor(sum, 4);
+        if ((lane & 7) == 0 && g < G) xs_s[wave][g] = sum;
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -219,9 +257,18 @@ __global__ __launch_bounds__(256) void scan_scatter_kernel(ScatterArgs a) {
   const int E = a.E, P = a.T * a.k;
   const int chunk = blockIdx.x;
   const int n_chunks = (P + kChunkPairs - 1) / kChunkPairs;
+  // this wave's pair ids, loaded before the scan so both round trips overlap
+  const int p0 = chunk * kChunkPairs + wave * 256;
+  int pe[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int p = p0 + r * 64 + lane;
+    pe[r] = p < P ? a.topk_idx[p] : 0;
+  }
   // totals and this chunk's base per expert
   int tot = 0, before = 0;
   if (tid < E) {
+#pragma unroll 8
     for (int c = 0; c < n_chunks; ++c) {
       const int v = a.chunk_hist[c * E + tid];
       tot += v;
@@ -265,10 +312,9 @@ __global__ __launch_bounds__(256) void scan_scatter_kernel(ScatterArgs a) {
   // wave-level counts of this chunk's pairs: wave w owns 256 consecutive pairs
   for (int i = tid; i < 4 * 256; i += 256) (&wbase[0][0])[i] = 0;
   __syncthreads();
-  const int p0 = chunk * kChunkPairs + wave * 256;
   for (int r = 0; r < 4; ++r) {
     const int p = p0 + r * 64 + lane;
-    if (p < P) atomicAdd(&wbase[wave][a.topk_idx[p]], 1);
+    if (p < P) atomicAdd(&wbase[wave][pe[r]], 1);
   }
   __syncthreads();
   if (tid < E) {
@@ -284,7 +330,7 @@ __global__ __launch_bounds__(256) void scan_scatter_kernel(ScatterArgs a) {
   for (int r = 0; r < 4; ++r) {
     const int p = p0 + r * 64 + lane;
     if (p < P) {
-      const int e = a.topk_idx[p];
+      const int e = pe[r];
       const uint64_t peers = match_any((uint32_t)e, 8);
       const int rank = __popcll(peers & lanemask_lt());
       const int pos = wbase[wave][e] + rank;
