@@ -14,7 +14,7 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   roofline      the dominant kernel (gate/up GEMM): algorithmic bytes or
                 flops per launch / its mean duration from HIP events recorded
                 on the library's stream around every launch in the timed region
-  cpu_baseline  the CPU oracle timed on this host on the same 512 tokens
+  cpu_baseline  the CPU oracle timed on this host on the same workload
   secondary     the 2048-token Zipf-skewed prefill (bf16 MFMA fraction) and
                 batch-1 decode (HBM GB/s of the GEMV kernels), same method
 """
@@ -35,8 +35,8 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer prefill tokens/s at T=512/2048 + % bf16 MFMA peak; decode HBM GB/s"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2516.6
-PREFILL_KERNELS = ["router", "topk", "scan_scatter", "gemm_gateup", "gemm_down_routed",
-                   "gemm_down_shared_combine"]
+PREFILL_KERNELS = ["router", "topk", "scan_scatter", "gemm_gateup", "gemm_down", "combine"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gateup_prefill_t512.json")
 DECODE_KERNELS = ["decode_router", "decode_gateup", "decode_down", "decode_combine"]
 
 
@@ -156,16 +156,38 @@ def run_decode(name, steps, warmup, copies):
                 end_to_end_gbs=(gemv_bytes + router_bytes) / (ms_step / 1e3) / 1e9)
 
 
-def cpu_baseline(w, x, tokens):
+def cpu_baseline(w, x, min_seconds=10.0):
+    """The CPU oracle on the same workload: whole passes over all T tokens,
+    repeated until at least `min_seconds` have elapsed."""
     import oracle
-    sample = np.arange(min(tokens, x.shape[0]))
+    T = x.shape[0]
+    passes = 0
     t0 = time.perf_counter()
-    oracle.layer(x, w, tokens=sample)
-    dt = time.perf_counter() - t0
-    return {"value": len(sample) / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
-            "kind": "oracle", "sample": f"first {len(sample)} of the {x.shape[0]} tokens of the "
-            f"same workload, whole layer (router, top-8, 8 routed + shared SwiGLU experts), "
+    while True:
+        oracle.layer(x, w)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": passes * T / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "sample": f"{passes} full pass(es) over the {T} tokens of the same "
+            f"workload (router, top-8, 8 routed + shared SwiGLU experts, fp64 accumulation), "
             f"{dt:.1f} s wall"}
+
+
+def measured_traffic(workload):
+    """HBM bytes per gate/up launch from the committed FETCH_SIZE / WRITE_SIZE
+    summary, or None when it is missing, for another workload, or taken from
+    different kernel sources."""
+    from int4_grouped_gemm_router_amd import profiling
+    if workload != "prefill_t512" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("sources_sha256") != profiling.sources_digest():
+        log("traffic summary is stale (kernel sources changed since the counters were taken)")
+        return None
+    return t["hbm_bytes_per_launch"]
 
 
 def main():
@@ -201,7 +223,8 @@ def main():
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     if "gateup_algorithmic_bytes" in res and gu_flops / res["gateup_algorithmic_bytes"] < ridge:
         roofline = {"bound": "hbm", "achieved": res["gateup_gbs"], "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": res["gateup_gbs"] / PEAK_HBM_GBS, "traffic": None,
+                    "unit": "GB/s", "frac": res["gateup_gbs"] / PEAK_HBM_GBS,
+                    "traffic": measured_traffic(args.workload),
                     "kernel": "gemm_gateup", "per_launch_bytes": res["gateup_algorithmic_bytes"],
                     "mean_us": gu_us}
     else:
@@ -224,7 +247,7 @@ def main():
         "mfma_frac_layer": res["mfma_frac_layer"],
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, x, res["T"])
+        out["cpu_baseline"] = cpu_baseline(w, x)
         log(f"cpu baseline: {out['cpu_baseline']}")
     if not args.no_secondary:
         sec = []

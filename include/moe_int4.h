@@ -28,7 +28,7 @@
  *  - Return value: MOE_OK (0) or a negative MOE_E* code. Arguments are checked
  *    before anything is enqueued, so on error nothing has been launched.
  *  - Supported dims: E <= 256 and E % 64 == 0, top_k == 8, block_m == 32,
- *    H % 256 == 0 (H <= 8192), I % 128 == 0 (I <= 4096).
+ *    H % 256 == 0 (H <= 4096), I % 128 == 0 (I <= 4096).
  */
 #ifndef MOE_INT4_H
 #define MOE_INT4_H

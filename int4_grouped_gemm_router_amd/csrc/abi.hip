@@ -11,7 +11,7 @@ namespace {
 
 bool dims_ok(const moe_dims* d) {
   return d && d->E > 0 && d->E <= 256 && d->E % 64 == 0 && d->top_k == 8 && d->block_m == 32 &&
-         d->H > 0 && d->H % 256 == 0 && d->H <= 8192 && d->I > 0 && d->I % 128 == 0 &&
+         d->H > 0 && d->H % 256 == 0 && d->H <= 4096 && d->I > 0 && d->I % 128 == 0 &&
          d->I <= 4096;
 }
 
@@ -54,7 +54,7 @@ struct PrefillWs {
   int32_t *topk_idx, *chunk_hist, *hist, *offsets, *perm, *inv_perm, *block_map, *num_blocks;
   int32_t *items, *num_items;
   float* topk_w;
-  uint16_t *xs3, *h, *hs3;
+  uint16_t* h;  // [(k+1)Tc][I]
   float* partial;
 };
 
@@ -65,7 +65,6 @@ PrefillWs carve_prefill(const moe_dims* d, int Tc, void* ws, size_t* bytes) {
   for (int T = 1; T <= Tc; ++T)
     logit_elems = std::max(logit_elems, (size_t)router_splits(d, T) * T * d->E);
   const int k = d->top_k;
-  const int Kx_gu = extra_k(d->H / kGroup), Kx_d = extra_k(d->I / kGroup);
   w.logit_partial = c.take<float>(logit_elems);
   w.topk_idx = c.take<int32_t>((size_t)k * Tc);
   w.topk_w = c.take<float>((size_t)k * Tc);
@@ -78,9 +77,7 @@ PrefillWs carve_prefill(const moe_dims* d, int Tc, void* ws, size_t* bytes) {
   w.num_blocks = c.take<int32_t>(1);
   w.items = c.take<int32_t>(3 * (size_t)max_items(d, Tc));
   w.num_items = c.take<int32_t>(1);
-  w.xs3 = c.take<uint16_t>((size_t)Tc * Kx_gu);
   w.h = c.take<uint16_t>((size_t)(k + 1) * Tc * d->I);
-  w.hs3 = c.take<uint16_t>((size_t)(k + 1) * Tc * Kx_d);
   w.partial = c.take<float>((size_t)(k + 1) * Tc * d->H);
   *bytes = c.used;
   return w;
@@ -188,7 +185,6 @@ int moe_route(const moe_dims* dims, const float* logits, int32_t T, const moe_ro
   ta.T = T;
   ta.E = dims->E;
   ta.k = dims->top_k;
-  ta.H = dims->H;
   if (launch_topk(ta, s) != hipSuccess) return MOE_EHIP;
   ScatterArgs sa{};
   sa.topk_idx = out->topk_idx;
@@ -251,7 +247,6 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
   const PrefillWs W = carve_prefill(dims, Tc, ws, &need);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int H = dims->H, I = dims->I, E = dims->E, k = dims->top_k;
-  const int Kx_gu = extra_k(H / kGroup), Kx_d = extra_k(I / kGroup);
   const PackGeom gu = pack_geom(I, H, 1), dn = pack_geom(H, I, 0);
   const uint8_t* planes = static_cast<const uint8_t*>(w->router_w3) + kHeaderBytes;
 
@@ -277,13 +272,9 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
     ta.topk_idx = topk_idx;
     ta.topk_w = topk_w;
     ta.chunk_hist = W.chunk_hist;
-    ta.x = xc;
-    ta.xs3 = W.xs3;
     ta.T = Tn;
     ta.E = E;
     ta.k = k;
-    ta.H = H;
-    ta.Kx = Kx_gu;
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;
     if (launch_topk(ta, s) != hipSuccess) return MOE_EHIP;
 
@@ -308,17 +299,12 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
     GemmArgs g{};
     g.items = W.items;
     g.num_items = W.num_items;
+    g.shared_slots = (Tn + kItemRows - 1) / kItemRows;
     g.T = Tn;
     g.k = k;
     g.perm = sa.perm;
-    g.topk_w = topk_w;
-    const int routed = max_items(dims, Tn), shared = (Tn + kItemRows - 1) / kItemRows;
 
     // gate/up + SwiGLU (routed and shared items in one launch)
-    g.routed_slots = routed;
-    g.shared_slots = shared;
-    g.total_slots = round_up(routed + shared, 8);
-    g.n_tiles = gu.n_wt / 4;
     g.blob = static_cast<const uint8_t*>(w->experts_gate_up) + kHeaderBytes;
     g.shared_blob = static_cast<const uint8_t*>(w->shared_gate_up) + kHeaderBytes;
     g.expert_bytes = gu.expert_bytes;
@@ -326,19 +312,11 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
     g.K = H;
     g.paired = 1;
     g.act = xc;
-    g.act3 = W.xs3;
-    g.Kx = Kx_gu;
     g.h_out = W.h;
-    g.hs3_out = W.hs3;
-    g.Kx_down = Kx_d;
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;
     if (launch_gemm(kGateUp, g, s) != hipSuccess) return MOE_EHIP;
 
-    // down: routed items (weighted per pair) and shared items in one launch
-    g.routed_slots = routed;
-    g.shared_slots = shared;
-    g.total_slots = round_up(routed + shared, 8);
-    g.n_tiles = dn.n_wt / 4;
+    // down: routed items (one output row per pair) and shared items in one launch
     g.blob = static_cast<const uint8_t*>(w->experts_down) + kHeaderBytes;
     g.shared_blob = static_cast<const uint8_t*>(w->shared_down) + kHeaderBytes;
     g.expert_bytes = dn.expert_bytes;
@@ -346,8 +324,7 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
     g.K = I;
     g.paired = 0;
     g.act = W.h;
-    g.act3 = W.hs3;
-    g.Kx = Kx_d;
+    g.h_out = nullptr;
     g.partial = W.partial;
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;
     if (launch_gemm(kDown, g, s) != hipSuccess) return MOE_EHIP;

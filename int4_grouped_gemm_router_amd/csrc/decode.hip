@@ -236,13 +236,11 @@ __global__ __launch_bounds__(512) void decode_gateup_kernel(DecodeArgs a) {
     const uint8_t* nib = ebase + geom.nib_off + (((int64_t)wt * G + g) * 128 + lane) * 16;
     const u32x4 w0 = *reinterpret_cast<const u32x4*>(nib);
     const u32x4 w1 = *reinterpret_cast<const u32x4*>(nib + 1024);
-    const u32x2 sc = *reinterpret_cast<const u32x2*>(
-        ebase + geom.scl_off + (((int64_t)wt * G + g) * 16 + c16) * 8);
-    const uint16_t* bia = reinterpret_cast<const uint16_t*>(ebase + geom.bia_off);
+    const u32x4 sbv = *reinterpret_cast<const u32x4*>(
+        ebase + geom.sb_off + (((int64_t)wt * G + g) * 16 + c16) * 16);
     const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    const float s[4] = {bf16lo(sc.x), bf16hi(sc.x), bf16lo(sc.y), bf16hi(sc.y)};
-    float b[4];
-    for (int ct = 0; ct < 4; ++ct) b[ct] = bf16f(bia[((int64_t)wt * kWaveCols + 16 * ct + c16) * geom.Gp + g]);
+    const float s[4] = {bf16lo(sbv.x), bf16hi(sbv.x), bf16lo(sbv.y), bf16hi(sbv.y)};
+    const float b[4] = {bf16lo(sbv.z), bf16hi(sbv.z), bf16lo(sbv.w), bf16hi(sbv.w)};
     for (int t = 0; t < T; ++t) {
       if (jslot[t] < 0) continue;
       const uint16_t* xr = a.x + (int64_t)t * H + g * kGroup + 8 * kb;
@@ -321,13 +319,11 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
     const uint8_t* nib = ebase + geom.nib_off + (((int64_t)wt * G + g) * 128 + lane) * 16;
     const u32x4 w0 = *reinterpret_cast<const u32x4*>(nib);
     const u32x4 w1 = *reinterpret_cast<const u32x4*>(nib + 1024);
-    const u32x2 sc = *reinterpret_cast<const u32x2*>(
-        ebase + geom.scl_off + (((int64_t)wt * G + g) * 16 + c16) * 8);
-    const uint16_t* bia = reinterpret_cast<const uint16_t*>(ebase + geom.bia_off);
+    const u32x4 sbv = *reinterpret_cast<const u32x4*>(
+        ebase + geom.sb_off + (((int64_t)wt * G + g) * 16 + c16) * 16);
     const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    const float s[4] = {bf16lo(sc.x), bf16hi(sc.x), bf16lo(sc.y), bf16hi(sc.y)};
-    float b[4];
-    for (int ct = 0; ct < 4; ++ct) b[ct] = bf16f(bia[((int64_t)wt * kWaveCols + 16 * ct + c16) * geom.Gp + g]);
+    const float s[4] = {bf16lo(sbv.x), bf16hi(sbv.x), bf16lo(sbv.y), bf16hi(sbv.y)};
+    const float b[4] = {bf16lo(sbv.z), bf16hi(sbv.z), bf16lo(sbv.w), bf16hi(sbv.w)};
     for (int t = 0; t < T; ++t) {
       if (jslot[t] < 0) continue;
       const int row = jslot[t] == k ? k * T + t : t * k + jslot[t];

@@ -6,380 +6,528 @@
 // memory with fp32 accumulation and never writes expanded weights back; the
 // expert GEMMs are about 90% of prefill time.
 //
-// One work item is up to 64 rows of one expert (rows are (token, slot) pairs
-// in expert-sorted order, or tokens for the shared expert) and one 256-column
-// tile of the output; four waves each own 64 columns. Per 64-input group:
-//   - five groups are in flight per wave: the activation rows of a group,
-//     gathered through the routing permutation, arrive in an LDS ring by
-//     asynchronous global -> LDS copies; each wave's 2 KB of packed codes and
-//     128 B of scales arrive in a register ring as contiguous 1 KB wave loads;
-//     one barrier per group;
-//   - each code is expanded to the exact bf16 value 128 + q with two bit
-//     operations (no arithmetic);
-//   - the matrix cores form P = x . (128 + q) for the group in fp32 and the
-//     group's scale is applied on the accumulator: acc += s * P.
-// The bias term sum_g (b - 128 s) * sum_{c in g} x_c is added at the end by
-// three more matrix-core K-steps over precomputed per-group sums of the
-// activations (hi/lo bf16 halves) and the per-group (b - 128 s) (hi/lo).
-// Algebraically this is x . (q*s + b) with the weights used exactly.
+// A unit of work is one work item (up to 32 rows of one expert: (token, slot)
+// pairs in expert-sorted order, or 32 tokens of the shared expert) times one
+// column tile of the output; each wave owns 64 columns. The grid is
+// persistent: every block streams its units back to back and starts loading
+// the next unit while the current one finishes, so the memory pipeline does
+// not drain between units. Two kernels share the per-group arithmetic:
+//   gemm_ring_kernel    K a multiple of 512 (the main path): register ring of
+//                       plain loads, seven groups ahead, see below;
+//   gemm_stream_kernel  any other K: an LDS ring filled by asynchronous
+//                       global -> LDS copies with explicit vmcnt waits.
 //
-// The operands of the bias term are fetched in the prologue (so the
-// epilogue issues no global load): the (bias, scale) words of the lane's
-// groups into registers, the per-row group sums into LDS.
+// Per group and 16x16 output tile, with the codes expanded to the exact bf16
+// values 128 + q by two bit operations:
+//   P    = x . (128 + q)                      (matrix cores, fp32)
+//   xsum = x . 1                               (matrix cores: the rows' sums)
+//   acc += s * P + (b - 128 s) * xsum          (fp32 VALU)
+// Algebraically this is x . (q s + b) with the weights used exactly.
 //
-// Epilogues: gate/up -> h = silu(gate) * up rounded to bf16, plus the per-64
-// column sums of h for the down GEMM's bias term; down -> the output in fp32
-// at [token][slot]; the combine kernel then forms y = bf16(shared + sum over
-// the k slots of weight * output) in a fixed order, so the result is
-// deterministic.
+// Epilogues: gate/up -> h = silu(gate) * up rounded to bf16; down -> the
+// output in fp32 at [token][slot]; the combine kernel then forms
+// y = bf16(shared + sum over the k slots of weight * output) in a fixed order,
+// so the result is deterministic.
 #include "kernels.h"
 
 namespace moe {
 
-// Groups in flight: the packed codes and scales of a wave are private to it,
-// so they land in a register ring; the gathered activation rows are shared by
-// the block and land in an LDS ring through asynchronous global -> LDS copies.
-// kStages - 1 groups are in flight per wave (about 90 KB per CU at two blocks
-// per CU), which is what the memory system needs to stream near its peak.
-constexpr int kStages = 6;
-constexpr int kXStage = kItemRows * 128;        // gathered activations per group: 4 KB
-constexpr int kSub = kItemRows / 16;            // 16-row MFMA subtiles per item
+constexpr int kWaves = 8;                        // waves per block, 64 columns each
+constexpr int kThreads = kWaves * 64;
+constexpr int kBatch = 16;                       // units whose row tables a block stages at once
+constexpr int kXBytes = kItemRows * kGroup * 2;  // gathered activations per group: 4 KB
+constexpr int kCopiesPerStep = 4;                // copies per wave per group: x, 2 x codes, scale/bias
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Asynchronous 16-byte global -> LDS copy; lane l writes dst + 16 l.
+// Asynchronous global -> LDS copies; lane l writes dst + size * l.
 __device__ inline void dma16(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
 }
 
-// Wait until at most `groups` later load groups (XI + 3 loads each) are pending.
-template <int XI>
-__device__ inline void wait_groups(int groups) {
-  constexpr int per = XI + 3;
-  static_assert(kStages - 2 <= 4, "wait_groups covers up to four pending groups");
-  if (groups >= 4) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * per) : "memory");
-  } else if (groups == 3) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * per) : "memory");
-  } else if (groups == 2) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * per) : "memory");
-  } else if (groups == 1) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(per) : "memory");
-  } else {
+// Wait until at most n (a multiple of four, <= 24) of this wave's vector
+// memory operations are pending. Asynchronous copies complete in issue order
+// among themselves, so this guarantees every copy issued before the last n
+// copies has landed.
+__device__ inline void wait_vm(int n) {
+  if (n >= 24)
+    asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if (n >= 20)
+    asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+  else if (n >= 16)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (n >= 12)
+    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if (n >= 8)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (n >= 4)
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
 }
 
-constexpr int kMaxX3 = 96;                      // extra-K entries staged in LDS (fast path)
+// Keeps the compiler from moving LDS accesses across this point (the
+// epilogue transposes through LDS with differently typed accesses).
+__device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
 
-struct Lds {
-  u32x4 x[kStages][kXStage / 16];               // [stage][ms][c 8][row 16]
-  u32x4 x3[kMaxX3 / 8][64];                     // per-row group sums: [chunk][row]
-  int rowidx[kItemRows];
-  int outrow[kItemRows];
-  float red[4][kItemRows];
+struct UnitInfo {
+  int expert;  // -1: shared expert
+  int row0;    // first row (sorted pair position, or k*T + first token for the shared expert)
+  int rows;    // 1..kItemRows
+  int nt;      // column tile
 };
 
-// Main K loop, one 64-input group per step: wait for the group's loads, one
-// barrier (the activation stage is shared), issue the loads of the group
-// kStages - 1 ahead, expand the codes to bf16 and run the matrix cores.
-// XI = activation copies per wave per group (1 for items of up to 32 rows,
-// 2 for up to 64).
-template <int XI>
-__device__ inline void main_loop(const GemmArgs& a, Lds& L, int rows, int nsub,
-                                 const uint8_t* nib, const uint8_t* scl, f32x4 (&acc)[kSub][4]) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c16 = lane & 15, kb = lane >> 4;
-  const int K = a.K, G = K / kGroup;
-  // activation copies: instruction i of this wave covers units u = 64 (wave + 4 i) + lane
-  const uint16_t* xsrc[XI];
-#pragma unroll
-  for (int i = 0; i < XI; ++i) {
-    const int u = 64 * (wave + 4 * i) + lane;
-    const int m = (u >> 7) * 16 + (u & 15);
-    xsrc[i] = a.act + (int64_t)L.rowidx[m < rows ? m : 0] * K + 8 * ((u >> 4) & 7);
-  }
-  const uint8_t* nsrc = nib + lane * 16;
-  const uint8_t* ssrc = scl + c16 * 8;
-  const ExpandConsts xk = expand_consts();
-  u32x4 wq[kStages][2];
-  u32x2 sq[kStages];
-  auto issue = [&](int g, int slot) {
-#pragma unroll
-    for (int i = 0; i < XI; ++i) dma16(xsrc[i] + g * kGroup, &L.x[slot][64 * (wave + 4 * i)]);
-    wq[slot][0] = *reinterpret_cast<const u32x4*>(nsrc + (int64_t)g * kNibBytes);
-    wq[slot][1] = *reinterpret_cast<const u32x4*>(nsrc + (int64_t)g * kNibBytes + 1024);
-    sq[slot] = *reinterpret_cast<const u32x2*>(ssrc + (int64_t)g * kSclBytes);
-  };
-#pragma unroll
-  for (int d = 0; d < kStages - 1; ++d)
-    if (d < G) issue(d, d);
+template <int S>
+struct GemmLds {
+  u32x4 x[S][kXBytes / 16];             // [stage][ms 2][c 8][row 16]
+  u32x4 code[S][kWaves][2][64];         // [stage][wave][half][lane]
+  u32x4 sb[S][kWaves][16];              // [stage][wave][c16]: 4 scales, 4 biases
+  UnitInfo unit[kBatch];
+  int rowidx[kBatch][kItemRows];        // activation row of each item row
+  int outrow[kBatch][kItemRows];        // down: output row t*(k+1) + slot
+  u32x4 tr[kWaves][64];                 // per-wave epilogue transpose (1 KB)
+};
 
-  for (int g0 = 0; g0 < G; g0 += kStages) {
-#pragma unroll
-    for (int d = 0; d < kStages; ++d) {
-      const int g = g0 + d;
-      if (g >= G) break;
-      wait_groups<XI>(min(kStages - 2, G - 1 - g));
-      // Barrier that is also a compiler memory barrier: no LDS read of this
-      // stage may move above it and no copy into the stage freed by the
-      // previous step may move above it (a bare s_barrier builtin allows both).
-      lds_barrier();
-      if (g + kStages - 1 < G) issue(g + kStages - 1, (d + kStages - 1) % kStages);
-      const uint32_t words[8] = {wq[d][0].x, wq[d][0].y, wq[d][0].z, wq[d][0].w,
-                                 wq[d][1].x, wq[d][1].y, wq[d][1].z, wq[d][1].w};
-      const float s[4] = {bf16lo(sq[d].x), bf16hi(sq[d].x), bf16lo(sq[d].y), bf16hi(sq[d].y)};
-      u32x4 ax[2 * XI][2];
-#pragma unroll
-      for (int ms = 0; ms < 2 * XI; ++ms) {
-        ax[ms][0] = L.x[d][(ms * 8 + kb) * 16 + c16];
-        ax[ms][1] = L.x[d][(ms * 8 + 4 + kb) * 16 + c16];
-      }
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const u32x4 b0 = expand_codes(words[2 * ct], xk);
-        const u32x4 b1 = expand_codes(words[2 * ct + 1], xk);
-#pragma unroll
-        for (int ms = 0; ms < 2 * XI; ++ms) {
-          if (ms < nsub) {
-            f32x4 p = mfma16(ax[ms][0], b0, f32x4{0.f, 0.f, 0.f, 0.f});
-            p = mfma16(ax[ms][1], b1, p);
-            acc[ms][ct] += s[ct] * p;
-          }
-        }
-      }
-    }
-  }
-}
+// bf16 pairs (1.0, 1.0): the B operand that turns an MFMA into row sums.
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
 
-// B operand of the bias term for one lane: eight consecutive groups g0.. of
-// (b - 128 s) for its four columns, as truncated-bf16 heads (hi) and the bf16
-// of the remainders (lo).
-__device__ inline void bias_operands(const u32x4 (&bv)[4], const u32x2 (&sv)[8], u32x4 (&hi)[4],
-                                     u32x4 (&lo)[4]) {
+// One 64-input group for NS 16-row subtiles: the rows' group sums come from
+// the matrix cores (x . 1), then acc += s * P + (b - 128 s) * xsum.
+template <int NS>
+__device__ __forceinline__ void ring_step(const u32x4 w0, const u32x4 w1, const u32x4 sbv,
+                                          const u32x4* xst, int kb, int c16,
+                                          const ExpandConsts xk, f32x4 (&acc)[2][4]) {
+  const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  const float sc[4] = {bf16lo(sbv.x), bf16hi(sbv.x), bf16lo(sbv.y), bf16hi(sbv.y)};
+  const float bi[4] = {bf16lo(sbv.z), bf16hi(sbv.z), bf16lo(sbv.w), bf16hi(sbv.w)};
+  const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
+  u32x4 ax[NS][2];
+  f32x4 xsv[NS];
+#pragma unroll
+  for (int ms = 0; ms < NS; ++ms) {
+    ax[ms][0] = xst[(ms * 8 + kb) * 16 + c16];
+    ax[ms][1] = xst[(ms * 8 + 4 + kb) * 16 + c16];
+    xsv[ms] = mfma16(ax[ms][0], ones, f32x4{0.f, 0.f, 0.f, 0.f});
+    xsv[ms] = mfma16(ax[ms][1], ones, xsv[ms]);
+  }
+  f32x4 p[NS][4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    const uint32_t bw[4] = {bv[ct].x, bv[ct].y, bv[ct].z, bv[ct].w};
-    uint32_t h[4], l[4];
+    const u32x4 b0 = expand_codes(words[2 * ct], xk);
+    const u32x4 b1 = expand_codes(words[2 * ct + 1], xk);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      uint16_t hh[2], ll[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int o = 2 * d + e;
-        const float b = e ? bf16hi(bw[d]) : bf16lo(bw[d]);
-        const uint32_t sw = (ct < 2) ? sv[o].x : sv[o].y;
-        const float sc = (ct & 1) ? bf16hi(sw) : bf16lo(sw);
-        split_hi_lo(b - 128.0f * sc, hh[e], ll[e]);
-      }
-      h[d] = hh[0] | ((uint32_t)hh[1] << 16);
-      l[d] = ll[0] | ((uint32_t)ll[1] << 16);
+    for (int ms = 0; ms < NS; ++ms) {
+      p[ms][ct] = mfma16(ax[ms][0], b0, f32x4{0.f, 0.f, 0.f, 0.f});
+      p[ms][ct] = mfma16(ax[ms][1], b1, p[ms][ct]);
     }
-    hi[ct] = u32x4{h[0], h[1], h[2], h[3]};
-    lo[ct] = u32x4{l[0], l[1], l[2], l[3]};
+  }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const float bp = bi[ct] - 128.0f * sc[ct];
+#pragma unroll
+    for (int ms = 0; ms < NS; ++ms)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[ms][ct][i] = __builtin_fmaf(bp, xsv[ms][i], __builtin_fmaf(sc[ct], p[ms][ct][i], acc[ms][ct][i]));
   }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
+// ------------------------------------------------------------------ LDS-stream kernel
+//
+// The general path (any K that is a multiple of 128). One block of eight
+// waves per compute unit, 512 columns per unit. Per group the activation rows
+// (4 KB), each wave's codes (2 KB) and scale/bias words (256 B) arrive in an
+// S-stage LDS ring by asynchronous global -> LDS copies, S - 1 groups ahead
+// and across unit boundaries; no global load of the loop targets registers.
+template <int MODE, int S>
+__global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs a) {
+  __shared__ GemmLds<S> L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15, kb = lane >> 4;
-
-  // Block ids are dispatched round-robin over the 8 XCDs; keep the column
-  // tiles of one item on one XCD so its gathered rows are shared in L2.
-  const int bid = blockIdx.x;
-  const int q8 = bid >> 3;
-  const int slot = (q8 / a.n_tiles) * 8 + (bid & 7);
-  const int nt = q8 % a.n_tiles;
-
-  int expert = -1, row0 = 0, rows = 0, token0 = 0;
-  if (slot < a.routed_slots) {
-    if (slot >= *a.num_items) return;
-    expert = a.items[3 * slot];
-    row0 = a.items[3 * slot + 1];
-    rows = a.items[3 * slot + 2];
-  } else if (slot < a.routed_slots + a.shared_slots) {
-    token0 = (slot - a.routed_slots) * kItemRows;
-    rows = min(kItemRows, a.T - token0);
-    row0 = a.k * a.T + token0;
-  } else {
-    return;
-  }
-  if (rows <= 0) return;
-
   const int K = a.K, G = K / kGroup;
   const PackGeom geom = pack_geom(a.N, K, a.paired);
-  const int Gp = geom.Gp;
-  const int wt = nt * 4 + wave;
-  const uint8_t* ebase = expert >= 0 ? a.blob + (int64_t)expert * a.expert_bytes : a.shared_blob;
-  const uint8_t* nib = ebase + geom.nib_off + (int64_t)wt * G * kNibBytes;
-  const uint8_t* scl = ebase + geom.scl_off + (int64_t)wt * G * kSclBytes;
-  const uint8_t* bia = ebase + geom.bia_off;
+  const int n_wt = geom.n_wt;
+  const int n_tiles = (n_wt + kWaves - 1) / kWaves;
 
-  __shared__ Lds L;
+  // Blocks are dispatched round-robin over the 8 XCDs; the blocks of XCD x
+  // take the units of slots x, x+8, ..., so the column tiles of one item run
+  // on one XCD at about the same time and share its gathered rows in L2.
+  const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, nbx = gridDim.x >> 3;
+  const int ni = *a.num_items;
+  const int n_slots = ni + a.shared_slots;
+  const int slots_x = n_slots > xcd ? (n_slots - xcd + 7) >> 3 : 0;
+  const int units_x = slots_x * n_tiles;
+  const int my_units = units_x > lb ? (units_x - lb + nbx - 1) / nbx : 0;
+  const ExpandConsts xk = expand_consts();
 
-  // Row bookkeeping. The down GEMM's output row (token, slot) comes from the
-  // permutation; it is only needed by the epilogue, so its load stays in
-  // flight through the main loop.
-  int perm_p = 0;
-  if (tid < kItemRows) {
-    int ri = 0;
-    if (tid < rows) {
-      if (MODE == kGateUp) {
-        ri = expert >= 0 ? a.perm[row0 + tid] / a.k : token0 + tid;
+  // lane roles in the copies
+  const int xu = 32 * wave + (lane & 31);                         // 16-byte unit of the x stage
+  const int xm = (xu >> 7) * 16 + (xu & 15), xc = (xu >> 4) & 7;  // its row and chunk
+
+  for (int base = 0; base < my_units; base += kBatch) {
+    const int nb = min(kBatch, my_units - base);
+    lds_barrier();  // the previous batch is done with the tables
+    if (tid < nb) {
+      const int v = lb + (base + tid) * nbx;
+      const int slot = 8 * (v / n_tiles) + xcd;
+      UnitInfo u;
+      u.nt = v % n_tiles;
+      if (slot < ni) {
+        u.expert = a.items[3 * slot];
+        u.row0 = a.items[3 * slot + 1];
+        u.rows = a.items[3 * slot + 2];
       } else {
-        ri = row0 + tid;
-        if (expert >= 0) perm_p = a.perm[row0 + tid];
+        const int t0 = (slot - ni) * kItemRows;
+        u.expert = -1;
+        u.row0 = a.k * a.T + t0;
+        u.rows = min(kItemRows, a.T - t0);
       }
+      L.unit[tid] = u;
     }
-    L.rowidx[tid] = ri;
-  }
-  __syncthreads();
-
-  // Bias-term operands (fast path: every lane uses one run of eight groups,
-  // true for Gp <= 32 and Kx <= kMaxX3): the raw bias and scale loads are
-  // issued here and consumed after the main loop, and the per-row group
-  // sums of the activations are copied into LDS.
-  const bool fast = Gp <= 32 && a.Kx <= kMaxX3;
-  const int g0 = (8 * kb) % Gp;
-  u32x4 bv[4];
-  u32x2 sv[8];
-  if (fast) {
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-      bv[ct] = *reinterpret_cast<const u32x4*>(bia + (((int64_t)wt * kWaveCols + 16 * ct + c16) * Gp + g0) * 2);
-#pragma unroll
-    for (int o = 0; o < 8; ++o)
-      sv[o] = g0 + o < G ? *reinterpret_cast<const u32x2*>(scl + ((int64_t)(g0 + o) * 16 + c16) * 8)
-                         : u32x2{0u, 0u};
-    const int row = lane < rows ? lane : 0;  // lanes past the item copy row 0 (unused)
-    for (int c = wave; c < a.Kx / 8; c += 4)
-      dma16(a.act3 + (int64_t)L.rowidx[row] * a.Kx + 8 * c, &L.x3[c][0]);
-  }
-
-  const int nsub = (rows + 15) >> 4;
-  f32x4 acc[kSub][4];
-  for (int ms = 0; ms < kSub; ++ms)
-    for (int ct = 0; ct < 4; ++ct) acc[ms][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  main_loop<kItemRows / 32>(a, L, rows, nsub, nib, scl, acc);
-
-  // bias term: sum_g (b - 128 s)[col][g] * xsum[row][g], as extra K-steps
-  // (three segments of Gp entries: hi*hi, hi*lo, lo*hi; zero padding after)
-  if (fast) {
-    u32x4 hi[4], lo[4];
-    bias_operands(bv, sv, hi, lo);
-    for (int k0s = 0; k0s < a.Kx; k0s += 32) {
-      const int seg = (k0s + 8 * kb) / Gp;
-      u32x4 be[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        be[ct] = seg == 1 ? lo[ct] : (seg < 3 ? hi[ct] : u32x4{0u, 0u, 0u, 0u});
-#pragma unroll
-      for (int ms = 0; ms < kSub; ++ms) {
-        if (ms < nsub) {
-          const u32x4 ax = L.x3[k0s / 8 + kb][ms * 16 + c16];
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct) acc[ms][ct] = mfma16(ax, be[ct], acc[ms][ct]);
+    lds_barrier();
+    for (int e = tid; e < nb * kItemRows; e += kThreads) {
+      const int j = e / kItemRows, m = e % kItemRows;
+      const UnitInfo u = L.unit[j];
+      const int mm = m < u.rows ? m : 0;  // rows past the item copy row 0 (never stored)
+      if (MODE == kGateUp) {
+        L.rowidx[j][m] = u.expert >= 0 ? a.perm[u.row0 + mm] / a.k : u.row0 - a.k * a.T + mm;
+      } else {
+        L.rowidx[j][m] = u.row0 + mm;
+        int orow;
+        if (u.expert >= 0) {
+          const int p = a.perm[u.row0 + mm];
+          orow = p + p / a.k;  // row t*(k+1) + j of pair p = t*k + j
+        } else {
+          orow = (u.row0 - a.k * a.T + mm) * (a.k + 1) + a.k;
         }
+        L.outrow[j][m] = orow;
       }
     }
-  } else {
-    for (int k0s = 0; k0s < a.Kx; k0s += 32) {
-      const int k0 = k0s + 8 * kb;
-      const int seg = k0 / Gp, gg0 = k0 % Gp;
-      u32x4 be[4];
-      for (int ct = 0; ct < 4; ++ct) be[ct] = u32x4{0u, 0u, 0u, 0u};
-      if (seg < 3) {
-        u32x4 b8[4];
-        u32x2 s8[8];
-        for (int ct = 0; ct < 4; ++ct)
-          b8[ct] = *reinterpret_cast<const u32x4*>(bia + (((int64_t)wt * kWaveCols + 16 * ct + c16) * Gp + gg0) * 2);
-        for (int o = 0; o < 8; ++o)
-          s8[o] = gg0 + o < G ? *reinterpret_cast<const u32x2*>(scl + ((int64_t)(gg0 + o) * 16 + c16) * 8)
-                              : u32x2{0u, 0u};
-        u32x4 hi[4], lo[4];
-        bias_operands(b8, s8, hi, lo);
-        for (int ct = 0; ct < 4; ++ct) be[ct] = seg == 1 ? lo[ct] : hi[ct];
-      }
-#pragma unroll
-      for (int ms = 0; ms < kSub; ++ms) {
-        if (ms < nsub) {
-          const int m = ms * 16 + c16;
-          u32x4 ax = u32x4{0u, 0u, 0u, 0u};
-          if (m < rows)
-            ax = *reinterpret_cast<const u32x4*>(a.act3 + (int64_t)L.rowidx[m] * a.Kx + k0);
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct) acc[ms][ct] = mfma16(ax, be[ct], acc[ms][ct]);
-        }
-      }
-    }
-  }
+    lds_barrier();
 
-  if (MODE == kGateUp) {
-    const int I = a.N;
-    float hs[kSub][4];
+    // ---- copy side: unit iu, group ig
+    const int total = nb * G;
+    int iu = 0, ig = 0;
+    const uint16_t* xsrc = nullptr;
+    const uint8_t* nsrc = nullptr;
+    const uint8_t* bsrc = nullptr;
+    auto set_copy_unit = [&](int j) {
+      const int expert = __builtin_amdgcn_readfirstlane(L.unit[j].expert);
+      const int nt = __builtin_amdgcn_readfirstlane(L.unit[j].nt);
+      const int wt = min(nt * kWaves + wave, n_wt - 1);  // idle waves copy a valid tile
+      const uint8_t* eb = expert >= 0 ? a.blob + (int64_t)expert * a.expert_bytes : a.shared_blob;
+      nsrc = eb + geom.nib_off + (int64_t)wt * G * kNibBytes + lane * 16;
+      bsrc = eb + geom.sb_off + (int64_t)wt * G * kSbBytes + (lane & 15) * 16;
+      xsrc = a.act + (int64_t)L.rowidx[j][xm] * K + 8 * xc;
+    };
+    auto issue = [&](int st) {
+      if (lane < 32) dma16(xsrc + ig * kGroup, &L.x[st][32 * wave]);
+      dma16(nsrc + (int64_t)ig * kNibBytes, &L.code[st][wave][0][0]);
+      dma16(nsrc + (int64_t)ig * kNibBytes + 1024, &L.code[st][wave][1][0]);
+      if (lane < 16) dma16(bsrc + (int64_t)ig * kSbBytes, &L.sb[st][wave][0]);
+      if (++ig == G) {
+        ig = 0;
+        if (++iu < nb) set_copy_unit(iu);
+      }
+    };
+    set_copy_unit(0);
+    for (int d = 0; d < S - 1; ++d)
+      if (d < total) issue(d);
+
+    // ---- compute side: unit cu, group cg, stage st
+    f32x4 acc[2][4];
+    int cu = 0, cg = 0, st = 0;
+    int rows = 0, nsub = 0, nt = 0, row0 = 0;
+    bool active = false;
+    for (int s = 0; s < total; ++s) {
+      wait_vm(kCopiesPerStep * min(S - 2, total - 1 - s));
+      // all waves' copies of this group have landed, and every wave is done
+      // with the stage the next copies overwrite
+      lds_barrier();
+      if (s + S - 1 < total) issue(st == 0 ? S - 1 : st - 1);
+      if (cg == 0) {
+        rows = __builtin_amdgcn_readfirstlane(L.unit[cu].rows);
+        row0 = __builtin_amdgcn_readfirstlane(L.unit[cu].row0);
+        nt = __builtin_amdgcn_readfirstlane(L.unit[cu].nt);
+        nsub = (rows + 15) >> 4;
+        active = nt * kWaves + wave < n_wt;
 #pragma unroll
-    for (int ms = 0; ms < kSub; ++ms) {
-      for (int i = 0; i < 4; ++i) hs[ms][i] = 0.f;
-      if (ms < nsub) {
-        for (int ct = 0; ct < 2; ++ct) {
-          const int hc = 32 * wt + 16 * ct + c16;
-          for (int i = 0; i < 4; ++i) {
-            const int r = ms * 16 + 4 * kb + i;
-            const uint16_t hb = f2bf(silu(acc[ms][ct][i]) * acc[ms][ct + 2][i]);
-            if (r < rows) {
-              a.h_out[(int64_t)(row0 + r) * I + hc] = hb;
-              hs[ms][i] += bf16f(hb);
+        for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) acc[ms][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      if (active) {
+        const u32x4 w0 = L.code[st][wave][0][lane];
+        const u32x4 w1 = L.code[st][wave][1][lane];
+        const u32x4 sbv = L.sb[st][wave][c16];
+        const u32x4* xst = &L.x[st][0];
+        if (nsub == 2)
+          ring_step<2>(w0, w1, sbv, xst, kb, c16, xk, acc);
+        else
+          ring_step<1>(w0, w1, sbv, xst, kb, c16, xk, acc);
+      }
+
+      if (cg == G - 1) {
+        const int wt = nt * kWaves + wave;
+        if (MODE == kGateUp) {
+          const int I = a.N;
+          if (active) {
+            uint16_t* trb = reinterpret_cast<uint16_t*>(&L.tr[wave][0]);
+            const int rr = lane >> 2, ch = lane & 3;
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms) {
+              if (ms < nsub) {
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                  for (int i = 0; i < 4; ++i)
+                    trb[(4 * kb + i) * 32 + 16 * ct + c16] =
+                        f2bf(silu(acc[ms][ct][i]) * acc[ms][ct + 2][i]);
+                compiler_fence();
+                const u32x4 v = L.tr[wave][rr * 4 + ch];  // row rr of the 16 x 32 tile
+                compiler_fence();
+                if (16 * ms + rr < rows)
+                  *reinterpret_cast<u32x4*>(a.h_out + (int64_t)(row0 + 16 * ms + rr) * I + 32 * wt +
+                                            8 * ch) = v;
+              }
+            }
+          }
+        } else {
+          if (active) {
+            float* trf = reinterpret_cast<float*>(&L.tr[wave][0]);
+            const int rr = lane >> 2, c4 = lane & 3;
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms) {
+              if (ms < nsub) {
+                const int r = 16 * ms + rr;
+                const int orow = L.outrow[cu][r < rows ? r : 0];
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) trf[(4 * kb + i) * 16 + c16] = acc[ms][ct][i];
+                  compiler_fence();
+                  const f32x4 v = *reinterpret_cast<const f32x4*>(&trf[rr * 16 + 4 * c4]);
+                  compiler_fence();
+                  if (r < rows)
+                    *reinterpret_cast<f32x4*>(a.partial + (int64_t)orow * a.N + 64 * wt + 16 * ct +
+                                              4 * c4) = v;
+                }
+              }
             }
           }
         }
       }
-      for (int i = 0; i < 4; ++i) {
-        float v = hs[ms][i];
-        v += __shfl_xor(v, 1);
-        v += __shfl_xor(v, 2);
-        v += __shfl_xor(v, 4);
-        v += __shfl_xor(v, 8);
-        if (c16 == 0) L.red[wave][ms * 16 + 4 * kb + i] = v;
+      if (++cg == G) {
+        cg = 0;
+        ++cu;
+      }
+      if (++st == S) st = 0;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ register-ring kernel
+//
+// The main path for K a multiple of 512 (G % 8 == 0). Two blocks of four waves
+// per compute unit; each wave owns 64 columns. Every load of the loop is a
+// plain register load: per wave and group the packed codes (2 KB), a 1 KB
+// share of the gathered activation rows and a 256-byte share of the
+// scale/bias words are loaded into an eight-deep register ring seven groups
+// ahead (about 110 KB per compute unit in flight). At its turn a group's
+// activation and scale/bias shares are written to a two-stage LDS buffer, one
+// barrier, and all four waves read them. Unit boundaries fall on multiples of
+// eight groups, so every ring slot index is static and the loads for the next
+// unit start while the current one finishes. Loads of one kind complete in
+// order, so the compiler's own wait counts keep seven groups in flight (no
+// asynchronous LDS copies are mixed in, which would force full drains).
+
+constexpr int kRWaves = 4;
+constexpr int kRThreads = kRWaves * 64;
+constexpr int kRS = 8;  // ring depth in groups
+
+struct RingLds {
+  u32x4 x[2][kXBytes / 16];      // [stage][ms 2][c 8][row 16]
+  u32x4 sb[2][kRWaves][16];      // [stage][wave][c16]: 4 scales, 4 biases
+  UnitInfo unit[kBatch];
+  int rowidx[kBatch][kItemRows];
+  int outrow[kBatch][kItemRows];
+  u32x4 tr[kRWaves][64];
+};
+
+template <int MODE>
+__global__ __launch_bounds__(kRThreads, 2) void gemm_ring_kernel(GemmArgs a) {
+  __shared__ RingLds L;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, kb = lane >> 4;
+  const int K = a.K, G = K / kGroup;
+  const PackGeom geom = pack_geom(a.N, K, a.paired);
+  const int n_wt = geom.n_wt;
+  const int n_tiles = (n_wt + kRWaves - 1) / kRWaves;
+
+  const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, nbx = gridDim.x >> 3;
+  const int ni = *a.num_items;
+  const int n_slots = ni + a.shared_slots;
+  const int slots_x = n_slots > xcd ? (n_slots - xcd + 7) >> 3 : 0;
+  const int units_x = slots_x * n_tiles;
+  const int my_units = units_x > lb ? (units_x - lb + nbx - 1) / nbx : 0;
+  const ExpandConsts xk = expand_consts();
+
+  const int xu = 64 * wave + lane;                                 // 16-byte unit of the x stage
+  const int xm = (xu >> 7) * 16 + (xu & 15), xc = (xu >> 4) & 7;
+
+  for (int base = 0; base < my_units; base += kBatch) {
+    const int nb = min(kBatch, my_units - base);
+    lds_barrier();
+    if (tid < nb) {
+      const int v = lb + (base + tid) * nbx;
+      const int slot = 8 * (v / n_tiles) + xcd;
+      UnitInfo u;
+      u.nt = v % n_tiles;
+      if (slot < ni) {
+        u.expert = a.items[3 * slot];
+        u.row0 = a.items[3 * slot + 1];
+        u.rows = a.items[3 * slot + 2];
+      } else {
+        const int t0 = (slot - ni) * kItemRows;
+        u.expert = -1;
+        u.row0 = a.k * a.T + t0;
+        u.rows = min(kItemRows, a.T - t0);
+      }
+      L.unit[tid] = u;
+    }
+    lds_barrier();
+    for (int e = tid; e < nb * kItemRows; e += kRThreads) {
+      const int j = e / kItemRows, m = e % kItemRows;
+      const UnitInfo u = L.unit[j];
+      const int mm = m < u.rows ? m : 0;
+      if (MODE == kGateUp) {
+        L.rowidx[j][m] = u.expert >= 0 ? a.perm[u.row0 + mm] / a.k : u.row0 - a.k * a.T + mm;
+      } else {
+        L.rowidx[j][m] = u.row0 + mm;
+        int orow;
+        if (u.expert >= 0) {
+          const int p = a.perm[u.row0 + mm];
+          orow = p + p / a.k;
+        } else {
+          orow = (u.row0 - a.k * a.T + mm) * (a.k + 1) + a.k;
+        }
+        L.outrow[j][m] = orow;
       }
     }
-    __syncthreads();
-    const int Gd = I / kGroup, Gpd = round_up(Gd, 8);
-    if (tid < 128) {
-      const int w2 = tid >> 6, r = tid & 63;
-      if (r < rows) {
-        const float v = L.red[2 * w2][r] + L.red[2 * w2 + 1][r];
-        const int gh = nt * 2 + w2;
-        uint16_t hi, lo;
-        split_hi_lo(v, hi, lo);
-        uint16_t* o = a.hs3_out + (int64_t)(row0 + r) * a.Kx_down;
-        o[gh] = hi;
-        o[Gpd + gh] = hi;
-        o[2 * Gpd + gh] = lo;
+    lds_barrier();
+
+    // ---- load side: unit iu, group ig (stays on the last group once every
+    // group is issued, so each step issues the same four loads)
+    const int total = nb * G;  // a multiple of kRS
+    int iu = 0, ig = 0, issued = 0;
+    const uint16_t* xsrc = nullptr;
+    const uint8_t* nsrc = nullptr;
+    const uint8_t* bsrc = nullptr;
+    auto set_load_unit = [&](int j) {
+      const int expert = __builtin_amdgcn_readfirstlane(L.unit[j].expert);
+      const int nt = __builtin_amdgcn_readfirstlane(L.unit[j].nt);
+      const int wt = min(nt * kRWaves + wave, n_wt - 1);
+      const uint8_t* eb = expert >= 0 ? a.blob + (int64_t)expert * a.expert_bytes : a.shared_blob;
+      nsrc = eb + geom.nib_off + (int64_t)wt * G * kNibBytes + lane * 16;
+      bsrc = eb + geom.sb_off + (int64_t)wt * G * kSbBytes + lane * 4;
+      xsrc = a.act + (int64_t)L.rowidx[j][xm] * K + 8 * xc;
+    };
+    u32x4 rc[kRS][2], rx[kRS];
+    uint32_t rb[kRS];
+    auto load = [&](u32x4& c0, u32x4& c1, u32x4& xv, uint32_t& bv) {
+      c0 = *reinterpret_cast<const u32x4*>(nsrc + (int64_t)ig * kNibBytes);
+      c1 = *reinterpret_cast<const u32x4*>(nsrc + (int64_t)ig * kNibBytes + 1024);
+      xv = *reinterpret_cast<const u32x4*>(xsrc + ig * kGroup);
+      bv = *reinterpret_cast<const uint32_t*>(bsrc + (int64_t)ig * kSbBytes);
+      if (++issued < total) {
+        if (++ig == G) {
+          ig = 0;
+          set_load_unit(++iu);
+        }
       }
-    }
-    if (nt == 0) {
-      for (int e = tid; e < rows * a.Kx_down; e += 256) {
-        const int r = e / a.Kx_down, kk = e % a.Kx_down;
-        const int seg = kk / Gpd, g = kk % Gpd;
-        if (seg >= 3 || g >= Gd) a.hs3_out[(int64_t)(row0 + r) * a.Kx_down + kk] = 0;
-      }
-    }
-  } else {
-    if (tid < kItemRows)
-      L.outrow[tid] = expert >= 0 ? perm_p + perm_p / a.k  // row t*(k+1) + j
-                                  : (token0 + tid) * (a.k + 1) + a.k;
-    __syncthreads();
+    };
+    set_load_unit(0);
 #pragma unroll
-    for (int ms = 0; ms < kSub; ++ms) {
-      if (ms < nsub) {
-        for (int i = 0; i < 4; ++i) {
-          const int r = ms * 16 + 4 * kb + i;
-          if (r < rows) {
-            float* o = a.partial + (int64_t)L.outrow[r] * a.N + 64 * wt + c16;
-            for (int ct = 0; ct < 4; ++ct) o[16 * ct] = acc[ms][ct][i];
+    for (int d = 0; d < kRS - 1; ++d) load(rc[d][0], rc[d][1], rx[d], rb[d]);
+
+    f32x4 acc[2][4];
+    int rows = 0, nsub = 0, nt = 0, row0 = 0;
+    bool active = false;
+    for (int s0 = 0; s0 < total; s0 += kRS) {
+      const int cu = s0 / G, cg0 = s0 % G;
+      if (cg0 == 0) {
+        rows = __builtin_amdgcn_readfirstlane(L.unit[cu].rows);
+        row0 = __builtin_amdgcn_readfirstlane(L.unit[cu].row0);
+        nt = __builtin_amdgcn_readfirstlane(L.unit[cu].nt);
+        nsub = (rows + 15) >> 4;
+        active = nt * kRWaves + wave < n_wt;
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) acc[ms][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int d = 0; d < kRS; ++d) {
+        const int nx = (d + kRS - 1) % kRS;
+        load(rc[nx][0], rc[nx][1], rx[nx], rb[nx]);  // group s0 + d + 7 (or a repeat of the last)
+        L.x[d & 1][xu] = rx[d];
+        reinterpret_cast<uint32_t*>(&L.sb[d & 1][wave][0])[lane] = rb[d];
+        // this group's shares are in LDS, and every wave is done with the
+        // stage these writes replaced (read two groups ago)
+        lds_barrier();
+        if (active) {
+          const u32x4 sbv = L.sb[d & 1][wave][c16];
+          if (nsub == 2)
+            ring_step<2>(rc[d][0], rc[d][1], sbv, &L.x[d & 1][0], kb, c16, xk, acc);
+          else
+            ring_step<1>(rc[d][0], rc[d][1], sbv, &L.x[d & 1][0], kb, c16, xk, acc);
+        }
+      }
+      if (cg0 + kRS < G) continue;
+
+      // ---- epilogue of unit cu
+      const int wt = nt * kRWaves + wave;
+      if (!active) continue;
+      if (MODE == kGateUp) {
+        const int I = a.N;
+        uint16_t* trb = reinterpret_cast<uint16_t*>(&L.tr[wave][0]);
+        const int rr = lane >> 2, ch = lane & 3;
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) {
+          if (ms < nsub) {
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                trb[(4 * kb + i) * 32 + 16 * ct + c16] =
+                    f2bf(silu(acc[ms][ct][i]) * acc[ms][ct + 2][i]);
+            compiler_fence();
+            const u32x4 v = L.tr[wave][rr * 4 + ch];
+            compiler_fence();
+            if (16 * ms + rr < rows)
+              *reinterpret_cast<u32x4*>(a.h_out + (int64_t)(row0 + 16 * ms + rr) * I + 32 * wt + 8 * ch) = v;
+          }
+        }
+      } else {
+        float* trf = reinterpret_cast<float*>(&L.tr[wave][0]);
+        const int rr = lane >> 2, c4 = lane & 3;
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) {
+          if (ms < nsub) {
+            const int r = 16 * ms + rr;
+            const int orow = L.outrow[cu][r < rows ? r : 0];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) trf[(4 * kb + i) * 16 + c16] = acc[ms][ct][i];
+              compiler_fence();
+              const f32x4 v = *reinterpret_cast<const f32x4*>(&trf[rr * 16 + 4 * c4]);
+              compiler_fence();
+              if (r < rows)
+                *reinterpret_cast<f32x4*>(a.partial + (int64_t)orow * a.N + 64 * wt + 16 * ct + 4 * c4) = v;
+            }
           }
         }
       }
@@ -431,17 +579,16 @@ __global__ void test_dequant_kernel(const uint8_t* ebase, int N, int K, int pair
   const PackGeom geom = pack_geom(N, K, paired);
   const int G = geom.G;
   const uint8_t* nib = ebase + geom.nib_off + ((int64_t)wt * G + g) * kNibBytes + lane * 16;
-  const uint8_t* scl = ebase + geom.scl_off + (((int64_t)wt * G + g) * 16 + c16) * 8;
   const u32x4 w0 = *reinterpret_cast<const u32x4*>(nib);
   const u32x4 w1 = *reinterpret_cast<const u32x4*>(nib + 1024);
-  const u32x2 sc = *reinterpret_cast<const u32x2*>(scl);
+  const u32x4 sbv =
+      *reinterpret_cast<const u32x4*>(ebase + geom.sb_off + ((int64_t)wt * G + g) * kSbBytes + c16 * 16);
   const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-  const float s[4] = {bf16lo(sc.x), bf16hi(sc.x), bf16lo(sc.y), bf16hi(sc.y)};
-  const uint16_t* bia = reinterpret_cast<const uint16_t*>(ebase + geom.bia_off);
+  const float s[4] = {bf16lo(sbv.x), bf16hi(sbv.x), bf16lo(sbv.y), bf16hi(sbv.y)};
+  const float bi[4] = {bf16lo(sbv.z), bf16hi(sbv.z), bf16lo(sbv.w), bf16hi(sbv.w)};
   const ExpandConsts xk = expand_consts();
   for (int ct = 0; ct < 4; ++ct) {
     const int j = 16 * ct + c16;
-    const float b = bf16f(bia[((int64_t)wt * kWaveCols + j) * geom.Gp + g]);
     int mat = 0, row = 64 * wt + j;
     if (paired) {
       mat = j >> 5;
@@ -454,19 +601,48 @@ __global__ void test_dequant_kernel(const uint8_t* ebase, int N, int K, int pair
         for (int hlf = 0; hlf < 2; ++hlf) {
           const float e128 = hlf ? bf16hi(pairs[d]) : bf16lo(pairs[d]);
           const int kk = g * kGroup + 32 * ks + 8 * kb + 2 * d + hlf;
-          out[((int64_t)mat * N + row) * K + kk] = (e128 - 128.0f) * s[ct] + b;
+          out[((int64_t)mat * N + row) * K + kk] = (e128 - 128.0f) * s[ct] + bi[ct];
         }
     }
   }
 }
 
-hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t s) {
-  const dim3 grid(a.total_slots * a.n_tiles), block(256);
-  if (mode == kGateUp)
-    hipLaunchKernelGGL(gemm_kernel<kGateUp>, grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL(gemm_kernel<kDown>, grid, block, 0, s, a);
+namespace {
+
+// Persistent grid: one block per compute unit (a multiple of 8 for the XCD mapping).
+int persistent_blocks() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 8)
+      cus = 256;
+    cached[dev] = cus / 8 * 8;
+  }
+  return cached[dev];
+}
+
+template <int MODE>
+hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
+  const int G = a.K / kGroup;
+  if (G < 2 || G > kMaxGroups) return hipErrorInvalidValue;
+  const int cus = persistent_blocks();
+  if (G % kRS == 0) {
+    const dim3 grid(2 * cus), block(kRThreads);
+    hipLaunchKernelGGL(gemm_ring_kernel<MODE>, grid, block, 0, s, a);
+    return hipGetLastError();
+  }
+  const dim3 grid(cus), block(kThreads);
+  hipLaunchKernelGGL((gemm_stream_kernel<MODE, 6>), grid, block, 0, s, a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t s) {
+  return mode == kGateUp ? launch_mode<kGateUp>(a, s) : launch_mode<kDown>(a, s);
 }
 
 hipError_t launch_combine(const float* partial, const float* topk_w, uint16_t* y, int T, int N,

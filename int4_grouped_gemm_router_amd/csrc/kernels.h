@@ -12,7 +12,7 @@ namespace moe {
 
 constexpr int kChunkPairs = 1024;  // (token, slot) pairs per scatter block
 constexpr int kItemRows = 32;      // rows of one expert per GEMM work item (one routing block)
-constexpr int kMaxGroups = 128;    // H / 64 upper bound
+constexpr int kMaxGroups = 64;     // K / 64 upper bound of the expert GEMMs
 constexpr int kDecodeMaxT = 4;
 constexpr int kMaxSplits = 4;      // router K splits summed by the top-k kernel
 
@@ -24,9 +24,7 @@ struct TopkArgs {
   int32_t* topk_idx;      // [T][k]
   float* topk_w;          // [T][k]
   int32_t* chunk_hist;    // [chunks][E] (zeroed beforehand) or null
-  const uint16_t* x;      // [T][H] bf16 (for xs3)
-  uint16_t* xs3;          // [T][Kx] or null
-  int T, E, k, H, Kx;
+  int T, E, k;
 };
 
 struct ScatterArgs {
@@ -44,10 +42,7 @@ enum GemmMode { kGateUp = 0, kDown = 1 };
 struct GemmArgs {
   const int32_t* items;      // routed work list [max][3] (expert, first row, rows)
   const int32_t* num_items;  // device scalar
-  int routed_slots;          // grid slots reserved for routed items
-  int shared_slots;          // grid slots for shared items (kItemRows tokens each)
-  int total_slots;           // routed + shared, rounded up to a multiple of 8
-  int n_tiles;               // 256-column tiles per item (4 waves x 64 columns)
+  int shared_slots;          // shared-expert items (kItemRows tokens each)
   const uint8_t* blob;       // routed experts (past the header)
   const uint8_t* shared_blob;
   int64_t expert_bytes;
@@ -56,14 +51,9 @@ struct GemmArgs {
   int k;                     // experts per token
   // activations
   const uint16_t* act;       // gate/up: x [T][K]; down: h [(k+1)T][K]
-  const uint16_t* act3;      // gate/up: xs3 [T][Kx]; down: hs3 [(k+1)T][Kx]
-  int Kx;
   const int32_t* perm;       // [kT]
-  const float* topk_w;       // [kT]
   // outputs
-  uint16_t* h_out;           // gate/up: h [(k+1)T][N]
-  uint16_t* hs3_out;         // gate/up: hs3 [(k+1)T][Kx_down]
-  int Kx_down;
+  uint16_t* h_out;           // gate/up: h [(k+1)T][N] bf16
   float* partial;            // down: [T][k+1][N] fp32; slot j < k routed, slot k shared
 };
 

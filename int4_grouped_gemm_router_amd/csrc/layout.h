@@ -9,16 +9,16 @@
 // use the same (kb, element) -> k assignment, so the contraction is exact
 // whatever order the hardware walks K in.
 //
-// Per expert, three regions (byte offsets from the expert base):
+// Per expert, two regions (byte offsets from the expert base):
 //   nib  [wt][g][half 2][lane 64][16 B]  eight u32 words per lane, words
 //        0..3 in half 0 and 4..7 in half 1 (so each half is one contiguous
 //        1 KB wave load): word 2*ct + ks holds the codes of column 16*ct + c16
 //        for k = 64g + 32ks + 8kb + o, o = 0..7, code o at nibble position
 //        (o & 1) * 4 + (o >> 1); with that order ((w >> 4d) & 0x000F000F) |
 //        0x43004300 is the bf16 pair (128 + q[2d], 128 + q[2d+1]), d = 0..3.
-//   scl  [wt][g][c16 16][ct 4]   bf16 scale of column 16*ct + c16, group g.
-//   bia  [wt][col 64][Gp]        bf16 bias, groups contiguous per column, zero
-//                                padded from G to Gp = roundup(G, 8).
+//   sb   [wt][g][c16 16][8 bf16]  entries 0..3: scale of column 16*ct + c16
+//        (ct = 0..3), entries 4..7: bias of the same columns, group g; one
+//        16-byte word per (column slot, group), 256 B per (wave tile, group).
 // Column j of wave tile wt is matrix row 64*wt + j (one matrix), or, with two
 // matrices (gate, up) per expert, gate row 32*wt + j for j < 32 and up row
 // 32*wt + j - 32 for j >= 32, so a wave holds gate and up of the same 32
@@ -35,11 +35,11 @@ namespace moe {
 constexpr int kGroup = 64;          // inputs per quantisation group
 constexpr int kWaveCols = 64;       // output columns per wave tile
 constexpr int kNibBytes = 2048;     // packed codes per (wave tile, group)
-constexpr int kSclBytes = 128;      // scales per (wave tile, group)
+constexpr int kSbBytes = 256;       // scales + biases per (wave tile, group)
 constexpr int kHeaderBytes = 256;   // blob header
 constexpr uint32_t kMagic = 0x4734494Du;  // "MI4G"
 constexpr uint32_t kRouterMagic = 0x3346424Du;  // "MBF3"
-constexpr int kVersion = 1;
+constexpr int kVersion = 2;
 
 __host__ __device__ inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
 
@@ -47,8 +47,8 @@ struct PackGeom {
   int N, K, paired;
   int n_eff;   // output columns per expert (2N when paired)
   int n_wt;    // wave tiles per expert
-  int G, Gp;   // groups along K, padded to a multiple of 8
-  int64_t nib_off, scl_off, bia_off, expert_bytes;
+  int G;       // groups along K
+  int64_t nib_off, sb_off, expert_bytes;
 };
 
 __host__ __device__ inline PackGeom pack_geom(int N, int K, int paired) {
@@ -59,11 +59,9 @@ __host__ __device__ inline PackGeom pack_geom(int N, int K, int paired) {
   g.n_eff = paired ? 2 * N : N;
   g.n_wt = g.n_eff / kWaveCols;
   g.G = K / kGroup;
-  g.Gp = round_up(g.G, 8);
   g.nib_off = 0;
-  g.scl_off = (int64_t)g.n_wt * g.G * kNibBytes;
-  g.bia_off = g.scl_off + (int64_t)g.n_wt * g.G * kSclBytes;
-  int64_t end = g.bia_off + (int64_t)g.n_wt * kWaveCols * g.Gp * 2;
+  g.sb_off = (int64_t)g.n_wt * g.G * kNibBytes;
+  int64_t end = g.sb_off + (int64_t)g.n_wt * g.G * kSbBytes;
   g.expert_bytes = (end + 255) / 256 * 256;
   return g;
 }
@@ -75,10 +73,6 @@ __host__ __device__ inline int64_t nib_word(int wt, int g, int lane, int u, int 
 
 // Nibble position of code o (0..7) inside its 32-bit word.
 __host__ __device__ inline int nibble_pos(int o) { return (o & 1) * 4 + (o >> 1); }
-
-// Extra K used to add the bias term through the matrix cores: three segments
-// of Gp entries (hi*hi, hi*lo, lo*hi cross terms), padded to a K-step of 32.
-__host__ __device__ inline int extra_k(int G) { return round_up(3 * round_up(G, 8), 32); }
 
 // Router planes: [plane 3][et E/64][g H/64][ct 4][ks 2][lane 64][8 bf16].
 __host__ __device__ inline int64_t router_index(int plane, int et, int g, int ct, int ks, int lane,

@@ -45,8 +45,7 @@ extern "C" int pack_int4_g64(const uint8_t* q0, const uint16_t* s0, const uint16
   for (int e = 0; e < count; ++e) {
     uint8_t* eb = base + kHeaderBytes + (int64_t)e * g.expert_bytes;
     uint32_t* nib = reinterpret_cast<uint32_t*>(eb + g.nib_off);
-    uint16_t* scl = reinterpret_cast<uint16_t*>(eb + g.scl_off);
-    uint16_t* bia = reinterpret_cast<uint16_t*>(eb + g.bia_off);
+    uint16_t* sb = reinterpret_cast<uint16_t*>(eb + g.sb_off);
     for (int wt = 0; wt < g.n_wt; ++wt) {
       for (int j = 0; j < kWaveCols; ++j) {
         // logical source of column j of this wave tile
@@ -67,8 +66,9 @@ extern "C" int pack_int4_g64(const uint8_t* q0, const uint16_t* s0, const uint16
         }
         const int ct = j >> 4, c16 = j & 15;
         for (int gi = 0; gi < g.G; ++gi) {
-          scl[(((int64_t)wt * g.G + gi) * 16 + c16) * 4 + ct] = s[(int64_t)row * g.G + gi];
-          bia[((int64_t)wt * kWaveCols + j) * g.Gp + gi] = b[(int64_t)row * g.G + gi];
+          uint16_t* sbw = sb + (((int64_t)wt * g.G + gi) * 16 + c16) * 8;
+          sbw[ct] = s[(int64_t)row * g.G + gi];
+          sbw[4 + ct] = b[(int64_t)row * g.G + gi];
           for (int ks = 0; ks < 2; ++ks)
             for (int kb = 0; kb < 4; ++kb) {
               const int lane = kb * 16 + c16;

@@ -11,9 +11,8 @@
 //   router_mfma   logits partials: x (bf16) * Wr (three exact bf16 planes)
 //                 on the matrix cores, fp32 accumulation, split along H
 //   topk          per token: sum of the partials (+ router bias), top-k with
-//                 ties to the lower index, renormalised softmax weights,
-//                 per-64 group sums of x (for the bias term of the expert
-//                 GEMM), and per-chunk expert counts
+//                 ties to the lower index, renormalised softmax weights and
+//                 per-chunk expert counts
 //   scan_scatter  per chunk of 1024 pairs: expert offsets (exclusive scan),
 //                 the chunk's base per expert, a stable scatter of the pairs
 //                 (wave ballot peer matching), and, in block 0, the histogram,
@@ -111,12 +110,9 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
-  __shared__ float xs_s[4][kMaxGroups];
   if (t >= a.T) return;
   const int E = a.E, k = a.k, per = E / 64;
-  // all partial loads first (splits <= kMaxSplits), then a fixed-order sum;
-  // the activation loads for the group sums are issued with them so that
-  // the two round trips overlap
+  // all partial loads first (splits <= kMaxSplits), then a fixed-order sum
   float pv[kMaxSplits][4];
 #pragma unroll
   for (int sp = 0; sp < kMaxSplits; ++sp)
@@ -124,16 +120,6 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     for (int i = 0; i < 4; ++i)
       pv[sp][i] = (sp < a.splits && i < per) ? a.partial[((int64_t)sp * a.T + t) * E + lane + 64 * i]
                                              : 0.f;
-  constexpr int kXPre = 4;  // group-sum loads issued up front: H <= 2048
-  const int G = a.H / kGroup;
-  const uint16_t* xrow = a.xs3 ? a.x + (int64_t)t * a.H : nullptr;
-  u32x4 xv[kXPre];
-#pragma unroll
-  for (int u = 0; u < kXPre; ++u) {
-    const int g = 8 * u + (lane >> 3);
-    xv[u] = (xrow && g < G) ? *reinterpret_cast<const u32x4*>(xrow + g * kGroup + 8 * (lane & 7))
-                            : u32x4{0u, 0u, 0u, 0u};
-  }
   float l[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -185,45 +171,6 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     a.topk_idx[pair] = sel_e;
     a.topk_w[pair] = p / z;
     if (a.chunk_hist) atomicAdd(&a.chunk_hist[(pair / kChunkPairs) * E + sel_e], 1);
-  }
-  // per-group sums of x for the expert GEMM's bias term
-  if (a.xs3) {
-    const int Gp = round_up(G, 8);
-    for (int gb = 0; gb < G; gb += 8 * kXPre) {
-      u32x4 v[kXPre];
-#pragma unroll
-      for (int u = 0; u < kXPre; ++u) {
-        const int g = gb + 8 * u + (lane >> 3);
-        if (gb == 0)
-          v[u] = xv[u];
-        else
-          v[u] = g < G ? *reinterpret_cast<const u32x4*>(xrow + g * kGroup + 8 * (lane & 7))
-                       : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int u = 0; u < kXPre; ++u) {
-        const int g = gb + 8 * u + (lane >> 3);
-        float sum = bf16lo(v[u].x) + bf16hi(v[u].x) + bf16lo(v[u].y) + bf16hi(v[u].y) +
-                    bf16lo(v[u].z) + bf16hi(v[u].z) + bf16lo(v[u].w) + bf16hi(v[u].w);
-        sum += __shfl_xor(sum, 1);
-        sum += __shfl_xor(sum, 2);
-        sum += __shfl_xor(sum, 4);
-        if ((lane & 7) == 0 && g < G) xs_s[wave][g] = sum;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    uint16_t* out = a.xs3 + (int64_t)t * a.Kx;
-    for (int kk = lane; kk < a.Kx; kk += 64) {
-      const int seg = kk / Gp, g = kk % Gp;
-      uint16_t v = 0;
-      if (seg < 3 && g < G) {
-        uint16_t hi, lo;
-        split_hi_lo(xs_s[wave][g], hi, lo);
-        v = seg == 2 ? lo : hi;
-      }
-      out[kk] = v;
-    }
   }
 }
 

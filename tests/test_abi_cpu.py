@@ -29,16 +29,16 @@ def test_library_exports_every_header_symbol():
 def _read_packed(blob, count, N, K, paired):
     """Recover (q, scale, bias) per matrix from a blob, following the layout
     documented in csrc/layout.h: per expert nib [wt][g][half][lane][4 words],
-    scl [wt][g][c16][ct], bia [wt][col][Gp]; codes o at nibble (o&1)*4 + o>>1."""
+    then sb [wt][g][c16][8 bf16] (four scales of columns 16*ct + c16, then
+    their four biases); codes o at nibble (o&1)*4 + o>>1."""
     hdr = np.frombuffer(blob[:32].tobytes(), dtype=np.int32)
-    assert hdr[0] == 0x4734494D and hdr[1] == 1
+    assert hdr[0] == 0x4734494D and hdr[1] == 2
     assert tuple(hdr[2:6]) == (count, N, K, int(paired))
     n_eff = 2 * N if paired else N
     n_wt, G = n_eff // 64, K // 64
-    Gp = -(-G // 8) * 8
     nib_bytes = n_wt * G * 2048
-    scl_bytes = n_wt * G * 128
-    end = nib_bytes + scl_bytes + n_wt * 64 * Gp * 2
+    sb_bytes = n_wt * G * 256
+    end = nib_bytes + sb_bytes
     ebytes = -(-end // 256) * 256
     nmat = 2 if paired else 1
     q = np.zeros((nmat, count, N, K), np.uint8)
@@ -49,17 +49,13 @@ def _read_packed(blob, count, N, K, paired):
         base = 256 + e * ebytes
         words = np.frombuffer(blob[base:base + nib_bytes].tobytes(), np.uint32).reshape(n_wt, G, 2, 64, 4)
         words = words.transpose(0, 1, 3, 2, 4).reshape(n_wt, G, 64, 8)
-        scl = np.frombuffer(blob[base + nib_bytes:base + nib_bytes + scl_bytes].tobytes(),
-                            np.uint16).reshape(n_wt, G, 16, 4)
-        bia = np.frombuffer(blob[base + nib_bytes + scl_bytes:base + end].tobytes(),
-                            np.uint16).reshape(n_wt, 64, Gp)
+        sb = np.frombuffer(blob[base + nib_bytes:base + end].tobytes(), np.uint16).reshape(n_wt, G, 16, 8)
         for wt in range(n_wt):
             for j in range(64):
                 mat, row = ((j // 32, 32 * wt + j % 32) if paired else (0, 64 * wt + j))
                 ct, c16 = j // 16, j % 16
-                s[mat, e, row] = scl[wt, :, c16, ct]
-                b[mat, e, row] = bia[wt, j, :G]
-                assert (bia[wt, j, G:] == 0).all()
+                s[mat, e, row] = sb[wt, :, c16, ct]
+                b[mat, e, row] = sb[wt, :, c16, 4 + ct]
                 for ks in range(2):
                     for kb in range(4):
                         w = words[wt, :, kb * 16 + c16, 2 * ct + ks]          # [G]
