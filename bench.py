@@ -7,7 +7,10 @@ seeded inputs already resident in HBM. One step = one call of
 moe_prefill_layer: router, top-k, routing metadata, grouped gate/up + SwiGLU,
 grouped down, shared expert and combine. Four copies of the packed weights
 (about 1.8 GB) are used in rotation so the weights stream from HBM rather
-than from the 256 MB Infinity Cache.
+than from the 256 MB Infinity Cache. The timed loop replays, step by step, a
+HIP graph of one layer call per weight copy; an eager pass over the same
+number of steps with HIP events around every launch gives the per-kernel
+times.
 
 Prints ONE JSON line on stdout (progress goes to stderr):
   value         tokens/s of the whole layer
@@ -61,7 +64,27 @@ def prefill_setup(name, copies, seed=0):
     return wl, w, x, xd, dws
 
 
+def _graph_of(calls):
+    """Capture `calls()` (layer launches on the current stream) into a HIP graph."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()                       # warm the allocator and code objects outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    torch.cuda.synchronize()
+    return g
+
+
 def run_prefill(name, steps, warmup, copies):
+    """Time `steps` layer calls. The step time (value) comes from replaying a
+    HIP graph of `copies` consecutive layer calls (one per weight copy); the
+    per-kernel durations come from HIP events recorded on the library's
+    stream around every launch of an eager pass over the same steps."""
     import torch
     from int4_grouped_gemm_router_amd import binding as B
     wl, w, x, xd, dws = prefill_setup(name, copies)
@@ -79,6 +102,9 @@ def run_prefill(name, steps, warmup, copies):
     hist = ro.hist.cpu().numpy()
     for i in range(warmup):
         B.moe_prefill_layer(d, dws[i % copies], xd, y, T, chunk, None, None, ws)
+    y_eager = y.clone()
+
+    # eager pass with events around every launch: per-kernel durations
     n_ev = 6 * chunks + 1
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
     arrays = [B._event_array(ev) for ev in events]
@@ -87,18 +113,35 @@ def run_prefill(name, steps, warmup, copies):
     for i in range(steps):
         B.moe_prefill_layer_profiled(d, dws[i % copies], xd, y, T, chunk, arrays[i], ws=ws)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_eager = time.perf_counter() - t0
     per = np.zeros((steps, 6 * chunks))
     for i in range(steps):
         for j in range(6 * chunks):
             per[i, j] = events[i][j].elapsed_time(events[i][j + 1])  # ms
     kern_ms = per.reshape(steps, chunks, 6).sum(axis=1).mean(axis=0) / chunks  # per launch
+
+    # timed region: exactly `steps` graph replays, one captured layer call per
+    # weight copy, replayed in rotation
+    graphs = [_graph_of(lambda i=i: B.moe_prefill_layer(d, dws[i], xd, y, T, chunk, None, None, ws))
+              for i in range(copies)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / steps
+    graph_ok = bool(torch.equal(y, y_eager))  # every weight copy holds the same values
+    if not graph_ok:
+        log(f"{name}: graph replay output differs from the eager output; reporting eager timing")
+        ms_step = wall_eager * 1e3 / steps
+
     U = int((hist > 0).sum()) if chunks == 1 else None
     gu_b, dn_b = expert_bytes(H, I)
     gate_up_flops = 2.0 * (wl.k + 1) * Tc * H * 2 * I
     expert_flops = T * (wl.k + 1) * 6.0 * H * I
     res = dict(workload=name, T=T, chunk=chunk, ms_per_step=ms_step, tokens_per_s=T / (ms_step / 1e3),
+               ms_per_step_eager=wall_eager * 1e3 / steps, graph_matches_eager=graph_ok,
                kernels_us={k: float(v * 1e3) for k, v in zip(PREFILL_KERNELS, kern_ms)},
                expert_tflops=expert_flops / (ms_step / 1e3) / 1e12)
     res["mfma_frac_layer"] = res["expert_tflops"] / PEAK_BF16_TFLOPS
@@ -240,7 +283,8 @@ def main():
         "config": {"workload": args.workload, "T": res["T"], "H": w.H, "I": w.I, "E": w.E,
                    "top_k": 8, "shared_experts": 1,
                    "weights": "int4 affine, groups of 64, bf16 scale+bias",
-                   "weight_copies": args.copies, "parallelism": "single GPU"},
+                   "weight_copies": args.copies, "launch": "hip graph per layer call",
+                   "parallelism": "single GPU"},
         "roofline": roofline,
         "kernels_us": res["kernels_us"],
         "expert_tflops": res["expert_tflops"],

@@ -270,9 +270,10 @@ __global__ __launch_bounds__(512) void decode_gateup_kernel(DecodeArgs a) {
     const int t = tid / 32, j = tid % 32;
     if (jslot[t] >= 0) {
       float gv = 0.f, uv = 0.f;
+      const int jg = 32 * (j >> 4) + (j & 15);  // gate column of intermediate j; up is 16 later
       for (int w = 0; w < kDecWaves; ++w) {
-        gv += red[w][t][j];
-        uv += red[w][t][32 + j];
+        gv += red[w][t][jg];
+        uv += red[w][t][jg + 16];
       }
       const int row = jslot[t] == k ? k * T + t : t * k + jslot[t];
       a.h[(int64_t)row * I + 32 * wt + j] = f2bf(silu(gv) * uv);

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
                   for (int i = 0; i < 4; ++i)
                     trb[(4 * kb + i) * 32 + 16 * ct + c16] =
-                        f2bf(silu(acc[ms][ct][i]) * acc[ms][ct + 2][i]);
+                        f2bf(silu(acc[ms][2 * ct][i]) * acc[ms][2 * ct + 1][i]);
                 compiler_fence();
                 const u32x4 v = L.tr[wave][rr * 4 + ch];  // row rr of the 16 x 32 tile
                 compiler_fence();
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(kRThreads, 2) void gemm_ring_kernel(GemmArgs a) {
 #pragma unroll
               for (int i = 0; i < 4; ++i)
                 trb[(4 * kb + i) * 32 + 16 * ct + c16] =
-                    f2bf(silu(acc[ms][ct][i]) * acc[ms][ct + 2][i]);
+                    f2bf(silu(acc[ms][2 * ct][i]) * acc[ms][2 * ct + 1][i]);
             compiler_fence();
             const u32x4 v = L.tr[wave][rr * 4 + ch];
             compiler_fence();
@@ -591,8 +591,8 @@ __global__ void test_dequant_kernel(const uint8_t* ebase, int N, int K, int pair
     const int j = 16 * ct + c16;
     int mat = 0, row = 64 * wt + j;
     if (paired) {
-      mat = j >> 5;
-      row = 32 * wt + (j & 31);
+      mat = (j >> 4) & 1;
+      row = 32 * wt + 16 * (j >> 5) + (j & 15);
     }
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4 v = expand_codes(words[2 * ct + ks], xk);

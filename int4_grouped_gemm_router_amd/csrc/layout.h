@@ -19,10 +19,12 @@
 //   sb   [wt][g][c16 16][8 bf16]  entries 0..3: scale of column 16*ct + c16
 //        (ct = 0..3), entries 4..7: bias of the same columns, group g; one
 //        16-byte word per (column slot, group), 256 B per (wave tile, group).
-// Column j of wave tile wt is matrix row 64*wt + j (one matrix), or, with two
-// matrices (gate, up) per expert, gate row 32*wt + j for j < 32 and up row
-// 32*wt + j - 32 for j >= 32, so a wave holds gate and up of the same 32
-// intermediate columns.
+// Column j = 16*ct + c16 of wave tile wt is matrix row 64*wt + j (one
+// matrix), or, with two matrices (gate, up) per expert, row
+// 32*wt + 16*(ct >> 1) + c16 of gate (ct even) or up (ct odd): each 16-column
+// tile of gate is followed by the up tile of the same 16 intermediate columns,
+// so any half wave tile (1 KB of codes per group) carries a complete SwiGLU
+// pair.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,7 +41,7 @@ constexpr int kSbBytes = 256;       // scales + biases per (wave tile, group)
 constexpr int kHeaderBytes = 256;   // blob header
 constexpr uint32_t kMagic = 0x4734494Du;  // "MI4G"
 constexpr uint32_t kRouterMagic = 0x3346424Du;  // "MBF3"
-constexpr int kVersion = 2;
+constexpr int kVersion = 3;
 
 __host__ __device__ inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
 

@@ -53,8 +53,8 @@ extern "C" int pack_int4_g64(const uint8_t* q0, const uint16_t* s0, const uint16
         const uint16_t *s, *b;
         int row;
         if (paired) {
-          const bool up = j >= 32;
-          row = 32 * wt + (j & 31);
+          const bool up = (j >> 4) & 1;
+          row = 32 * wt + 16 * (j >> 5) + (j & 15);
           q = (up ? q1 : q0) + e * mat;
           s = (up ? s1 : s0) + e * mats;
           b = (up ? b1 : b0) + e * mats;

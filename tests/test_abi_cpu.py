@@ -32,7 +32,7 @@ def _read_packed(blob, count, N, K, paired):
     then sb [wt][g][c16][8 bf16] (four scales of columns 16*ct + c16, then
     their four biases); codes o at nibble (o&1)*4 + o>>1."""
     hdr = np.frombuffer(blob[:32].tobytes(), dtype=np.int32)
-    assert hdr[0] == 0x4734494D and hdr[1] == 2
+    assert hdr[0] == 0x4734494D and hdr[1] == 3
     assert tuple(hdr[2:6]) == (count, N, K, int(paired))
     n_eff = 2 * N if paired else N
     n_wt, G = n_eff // 64, K // 64
@@ -52,7 +52,8 @@ def _read_packed(blob, count, N, K, paired):
         sb = np.frombuffer(blob[base + nib_bytes:base + end].tobytes(), np.uint16).reshape(n_wt, G, 16, 8)
         for wt in range(n_wt):
             for j in range(64):
-                mat, row = ((j // 32, 32 * wt + j % 32) if paired else (0, 64 * wt + j))
+                mat, row = (((j // 16) % 2, 32 * wt + 16 * (j // 32) + j % 16) if paired
+                            else (0, 64 * wt + j))
                 ct, c16 = j // 16, j % 16
                 s[mat, e, row] = sb[wt, :, c16, ct]
                 b[mat, e, row] = sb[wt, :, c16, 4 + ct]

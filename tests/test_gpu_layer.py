@@ -196,3 +196,38 @@ def test_decode_tiny_and_vs_prefill(torch_cuda):
     check_layer(x, w, yd, ld, *_route_of(md, 4))
     if np.array_equal(md["topk_idx"], mp["topk_idx"]):
         assert_y_close(synth.bf16_bits_to_f32(yd), synth.bf16_bits_to_f32(yp), "decode vs prefill")
+
+
+def test_prefill_graph_replay_matches_eager(torch_cuda):
+    """The layer captured in a HIP graph and replayed (with eager work and
+    synchronisations in between) gives exactly the eager output every time."""
+    torch = torch_cuda
+    wl, w, dw = _layer("prefill_t512")
+    _, _, x = synth.generate("prefill_t512", with_x=True)
+    d = dw.dims
+    T = x.shape[0]
+    xd = torch.from_numpy(x).cuda()
+    ws = B.workspace(d, T, B.MODE_PREFILL)
+    y_eager = torch.empty((T, d.H), dtype=torch.int16, device="cuda")
+    B.moe_prefill_layer(d, dw, xd, y_eager, T, 0, None, None, ws)
+    torch.cuda.synchronize()
+    y = torch.zeros_like(y_eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        B.moe_prefill_layer(d, dw, xd, y, T, 0, None, None, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.moe_prefill_layer(d, dw, xd, y, T, 0, None, None, ws)
+    for rep in range(3):
+        y.zero_()
+        ws.fill_(0xA5)                      # the workspace holds no state between calls
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {rep} differs from the eager output"
+        B.moe_prefill_layer(d, dw, xd, y, T, 0, None, None, ws)   # eager work in between
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager)
