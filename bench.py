@@ -156,6 +156,10 @@ def run_prefill(name, steps, warmup, copies):
 
 
 def run_decode(name, steps, warmup, copies):
+    """Batch-1 (or 4) decode: `steps` consecutive layer calls, each on fresh
+    activations, weights rotated over `copies` copies. The timed region
+    replays one HIP graph holding all `steps` calls; an eager pass with HIP
+    events around every launch gives the per-kernel times."""
     import torch
     from int4_grouped_gemm_router_amd import binding as B
     from int4_grouped_gemm_router_amd import synth
@@ -175,6 +179,7 @@ def run_decode(name, steps, warmup, copies):
     for i in range(min(steps, 64)):
         B.moe_decode_layer(d, dws[0], xd[warmup + i], y, T, None, ro, ws)
         hists.append(ro.hist.clone())
+    # eager pass with events: per-kernel durations
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     arrays = [B._event_array(ev) for ev in events]
     torch.cuda.synchronize()
@@ -182,10 +187,25 @@ def run_decode(name, steps, warmup, copies):
     for i in range(steps):
         B.moe_decode_layer_profiled(d, dws[i % copies], xd[warmup + i], y, T, arrays[i], ws=ws)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_eager = time.perf_counter() - t0
+    y_eager = y.clone()
     per = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(4)]
                     for i in range(steps)])
     kern_ms = per.mean(axis=0)
+    # timed region: one graph of all steps
+    def calls():
+        for i in range(steps):
+            B.moe_decode_layer(d, dws[i % copies], xd[warmup + i], y, T, None, None, ws)
+    g = _graph_of(calls)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    graph_ok = bool(torch.equal(y, y_eager))
+    if not graph_ok:
+        log(f"{name}: graph replay output differs from the eager output; reporting eager timing")
+        wall = wall_eager
     U = float(np.mean([(h.cpu().numpy() > 0).sum() for h in hists]))
     gu_b, dn_b = expert_bytes(H, I)
     gemv_bytes = (U + 1) * (gu_b + dn_b)
@@ -193,6 +213,7 @@ def run_decode(name, steps, warmup, copies):
     gemv_ms = float(kern_ms[1] + kern_ms[2])
     ms_step = wall * 1e3 / steps
     return dict(workload=name, T=T, steps=steps, ms_per_step=ms_step,
+                ms_per_step_eager=wall_eager * 1e3 / steps, graph_matches_eager=graph_ok,
                 unique_experts=U, kernels_us={k: float(v * 1e3) for k, v in zip(DECODE_KERNELS, kern_ms)},
                 gemv_bytes=gemv_bytes, gemv_gbs=gemv_bytes / (gemv_ms / 1e3) / 1e9,
                 step_bytes=gemv_bytes + router_bytes,

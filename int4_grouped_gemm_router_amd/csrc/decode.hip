@@ -5,11 +5,12 @@
 // batch 1 there is little weight reuse and memory bandwidth is the ceiling.
 // The pass therefore reads only the selected experts' packed weights, once
 // each (a token set that picks the same expert twice shares one read), with
-// coalesced 16-byte loads spread over many waves so enough bytes are in
-// flight; the arithmetic is plain fp32 on the vector ALUs.
+// coalesced 16-byte loads spread over many waves, each wave issuing all of
+// its loads at once; codes are expanded to exact bf16 (128 + q) and
+// multiplied by bf16 dot-product instructions with fp32 accumulation.
 //
 // Four launches on the caller's stream, no host synchronisation:
-//   decode_router   fp32 router logits, one wave per expert
+//   decode_router   fp32 router logits, one block per expert
 //   decode_gateup   top-k of every token (recomputed per block from the
 //                   logits), the unique selected experts in ascending order,
 //                   then gate/up + SwiGLU for (unique expert or shared expert)
@@ -26,17 +27,84 @@ namespace moe {
 namespace {
 
 constexpr int kDecWaves = 8;
+constexpr int kDecThreads = 64 * kDecWaves;
 
-// w = q*s + b applied to a lane's sixteen inputs: returns s * sum(x*q) + b * sum(x)
-// through the caller; here only sum(x*q) for one packed word (8 codes).
-__device__ inline float dot_codes(uint32_t w, const float* x8) {
-  float acc = 0.f;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
+                                         false);
+}
+
+// Order-preserving u32 key of an fp32 logit: NaN counts as -inf and -0 as +0,
+// so equal keys are exactly equal logits (ties then go to the lower index).
+__device__ inline uint32_t logit_key(float v) {
+  v = v == v ? v : -INFINITY;
+  if (v == 0.f) v = 0.f;
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Top-k (k <= 8) of one token's E <= 256 logits in one wave, in rank order
+// (logit descending, index ascending): lane j < k gets the j-th expert and
+// its logit. The k-th largest key is found bit by bit (a count of the keys at
+// or above each candidate per bit), then the selected keys are ranked.
+// `scratch` is this wave's 16-entry LDS area.
+__device__ void wave_topk(const float* __restrict__ row, int E, int k, int lane, uint32_t* scratch,
+                          int& sel_e, float& sel_l) {
+  const int per = E / 64;
+  uint32_t key[4];
 #pragma unroll
-  for (int o = 0; o < 8; ++o) {
-    const float q = (float)((w >> (4 * nibble_pos(o))) & 0xFu);
-    acc = fmaf(x8[o], q, acc);
+  for (int i = 0; i < 4; ++i) key[i] = i < per ? logit_key(row[lane + 64 * i]) : 0u;
+  uint32_t t = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(key[i] >= c));
+    if (cnt >= k) t = c;
   }
-  return acc;
+  // keys above t all belong to the top k; equal keys fill up by index
+  int need = k;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) need -= __popcll(__ballot(key[i] > t));
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint64_t eqm = __ballot(key[i] == t);
+    const int before = __popcll(eqm & lanemask_lt());
+    const bool sel = key[i] > t || (key[i] == t && before < need);
+    const int taken = min(need, __popcll(eqm));
+    need -= taken;
+    const uint64_t sm = __ballot(sel);
+    if (sel) {
+      const int pos = base + __popcll(sm & lanemask_lt());
+      scratch[pos] = key[i];
+      scratch[8 + pos] = (uint32_t)(lane + 64 * i);
+    }
+    base += __popcll(sm);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint32_t my_key = 0, my_e = 0;
+  int rank = 0;
+  if (lane < k) {
+    my_key = scratch[lane];
+    my_e = scratch[8 + lane];
+    for (int m = 0; m < k; ++m) {
+      const uint32_t km = scratch[m], em = scratch[8 + m];
+      rank += (km > my_key) || (km == my_key && em < my_e);
+    }
+  }
+  // lane j < k takes the entry of rank j
+  int src = 0;
+  for (int m = 0; m < k; ++m) {
+    const int rm = __shfl(rank, m);
+    if (rm == lane) src = m;
+  }
+  sel_e = (int)__shfl((int)my_e, src);
+  sel_l = row[sel_e < E ? sel_e : 0];
 }
 
 // Routing state every decode block needs, rebuilt from the logits.
@@ -48,47 +116,19 @@ struct DecodeRoute {
   int uniq[kDecodeMaxT * 8];
   int uniq_first[kDecodeMaxT * 8];  // first sorted position of each unique expert
   int n_uniq;
+  uint32_t scratch[kDecodeMaxT][16];
 };
 
-// Requires 256 <= blockDim.x; every thread must call it.
+// Requires kDecThreads threads; every thread must call it.
 __device__ void decode_route(const DecodeArgs& a, DecodeRoute& r) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = a.E, k = a.k, per = E / 64, P = a.T * k;
+  const int E = a.E, k = a.k, P = a.T * k;
   if (wave < a.T) {
     const int t = wave;
-    float l[4];
-    for (int i = 0; i < 4; ++i) {
-      const float v = i < per ? a.logits[(int64_t)t * E + lane + 64 * i] : -INFINITY;
-      l[i] = v == v ? v : -INFINITY;  // a NaN logit never wins; the selection stays valid
-    }
-    uint32_t taken = 0;
-    int sel = -1;
-    float sel_l = 0.f, top = 0.f;
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7FFFFFFF;
-      for (int i = 0; i < per; ++i) {
-        const int e = lane + 64 * i;
-        if (!((taken >> i) & 1u) && (l[i] > bv || (l[i] == bv && e < bi))) {
-          bv = l[i];
-          bi = e;
-        }
-      }
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (j == 0) top = bv;
-      if (lane == j) {
-        sel = bi;
-        sel_l = bv;
-      }
-    }
+    int sel;
+    float sel_l;
+    wave_topk(a.logits + (int64_t)t * E, E, k, lane, r.scratch[t], sel, sel_l);
+    const float top = __shfl(sel_l, 0);
     const float p = lane < k ? expf(sel_l - top) : 0.f;
     const float z = wave_sum(p);
     if (lane < k) {
@@ -131,46 +171,123 @@ __device__ void decode_route(const DecodeArgs& a, DecodeRoute& r) {
   __syncthreads();
 }
 
-}  // namespace
-
-// Grid: E/4 blocks of 256 threads; wave w computes expert 4*blockIdx.x + w.
-__global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = blockIdx.x * 4 + wave;
-  if (e >= a.E) return;
-  const float* wr = a.router_w + (int64_t)e * a.H;
-  float acc[kDecodeMaxT] = {0.f, 0.f, 0.f, 0.f};
-  for (int h0 = lane * 4; h0 < a.H; h0 += 256) {
-    const float4 w = *reinterpret_cast<const float4*>(wr + h0);
-    for (int t = 0; t < a.T; ++t) {
-      const u32x2 xv = *reinterpret_cast<const u32x2*>(a.x + (int64_t)t * a.H + h0);
-      acc[t] = fmaf(bf16lo(xv.x), w.x, acc[t]);
-      acc[t] = fmaf(bf16hi(xv.x), w.y, acc[t]);
-      acc[t] = fmaf(bf16lo(xv.y), w.z, acc[t]);
-      acc[t] = fmaf(bf16hi(xv.y), w.w, acc[t]);
-    }
-  }
-  for (int t = 0; t < a.T; ++t) {
-    float v = wave_sum(acc[t]);
-    if (a.rbias) v += a.rbias[e];
-    if (lane == 0) {
-      a.logits[(int64_t)t * a.E + e] = v;
-      if (a.logits_out) a.logits_out[(int64_t)t * a.E + e] = v;
+// Slot of token t in this block's expert (k for the shared expert), or -1.
+__device__ inline void token_slots(const DecodeRoute& r, int expert, int T, int k, int (&jslot)[kDecodeMaxT]) {
+#pragma unroll
+  for (int t = 0; t < kDecodeMaxT; ++t) {
+    jslot[t] = -1;
+    if (t < T) {
+      if (expert < 0) {
+        jslot[t] = k;
+      } else {
+        for (int j = 0; j < k; ++j)
+          if (r.sel_e[t][j] == expert) jslot[t] = j;
+      }
     }
   }
 }
 
-// Grid: (k*T + 1) slots x n_wt wave tiles; block: 512 threads (8 waves split K).
-__global__ __launch_bounds__(512) void decode_gateup_kernel(DecodeArgs a) {
+// Partial dot products of one lane for one group: the lane's 16 inputs of
+// the group (x0: k = 8kb.., x1: k = 32 + 8kb..) against its four columns'
+// codes; acc[ct] += s * sum(x (128 + q)) + (b - 128 s) * sum(x).
+__device__ inline void gemv_group(const u32x4 w0, const u32x4 w1, const u32x4 sbv, const u32x4 x0,
+                                  const u32x4 x1, const ExpandConsts xk, float (&acc)[4]) {
+  const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  const float sc[4] = {bf16lo(sbv.x), bf16hi(sbv.x), bf16lo(sbv.y), bf16hi(sbv.y)};
+  const float bi[4] = {bf16lo(sbv.z), bf16hi(sbv.z), bf16lo(sbv.w), bf16hi(sbv.w)};
+  constexpr uint32_t kOnes = 0x3F803F80u;
+  float xsum = 0.f;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) xsum = dot2(xs[d], kOnes, xsum);
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const u32x4 b0 = expand_codes(words[2 * ct], xk);
+    const u32x4 b1 = expand_codes(words[2 * ct + 1], xk);
+    float p = 0.f;
+    p = dot2(b0.x, xs[0], p);
+    p = dot2(b0.y, xs[1], p);
+    p = dot2(b0.z, xs[2], p);
+    p = dot2(b0.w, xs[3], p);
+    p = dot2(b1.x, xs[4], p);
+    p = dot2(b1.y, xs[5], p);
+    p = dot2(b1.z, xs[6], p);
+    p = dot2(b1.w, xs[7], p);
+    acc[ct] = __builtin_fmaf(bi[ct] - 128.0f * sc[ct], xsum, __builtin_fmaf(sc[ct], p, acc[ct]));
+  }
+}
+
+}  // namespace
+
+// Grid: E blocks of 256 threads; block e computes expert e's logit for every
+// token: each thread eight inputs per pass, then a block reduction in a fixed
+// order.
+__global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
+  __shared__ float part[4][kDecodeMaxT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e = blockIdx.x;
+  const float* wr = a.router_w + (int64_t)e * a.H;
+  float acc[kDecodeMaxT] = {0.f, 0.f, 0.f, 0.f};
+  for (int h0 = 8 * tid; h0 < a.H; h0 += 8 * 256) {
+    const float4 w0 = *reinterpret_cast<const float4*>(wr + h0);
+    const float4 w1 = *reinterpret_cast<const float4*>(wr + h0 + 4);
+    u32x4 xv[kDecodeMaxT];
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxT; ++t)
+      if (t < a.T) xv[t] = *reinterpret_cast<const u32x4*>(a.x + (int64_t)t * a.H + h0);
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxT; ++t) {
+      if (t < a.T) {
+        float v = acc[t];
+        v = fmaf(bf16lo(xv[t].x), w0.x, v);
+        v = fmaf(bf16hi(xv[t].x), w0.y, v);
+        v = fmaf(bf16lo(xv[t].y), w0.z, v);
+        v = fmaf(bf16hi(xv[t].y), w0.w, v);
+        v = fmaf(bf16lo(xv[t].z), w1.x, v);
+        v = fmaf(bf16hi(xv[t].z), w1.y, v);
+        v = fmaf(bf16lo(xv[t].w), w1.z, v);
+        v = fmaf(bf16hi(xv[t].w), w1.w, v);
+        acc[t] = v;
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kDecodeMaxT; ++t) {
+    const float v = wave_sum(acc[t]);
+    if (lane == 0) part[wave][t] = v;
+  }
+  __syncthreads();
+  if (tid < a.T) {
+    float v = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+    if (a.rbias) v += a.rbias[e];
+    a.logits[(int64_t)tid * a.E + e] = v;
+    if (a.logits_out) a.logits_out[(int64_t)tid * a.E + e] = v;
+  }
+}
+
+// Grid: (k*T + 1) slots x n_wt wave tiles; block: 8 waves that split K.
+// Slot < k*T: the slot-th unique selected expert (blocks past the number of
+// unique experts exit); slot k*T: the shared expert. The tokens' activations
+// are staged in LDS while the block recomputes the routing; then each wave
+// issues all of its groups' weight loads at once.
+template <int GPW>
+__global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a) {
   __shared__ DecodeRoute r;
   __shared__ float red[kDecWaves][kDecodeMaxT][kWaveCols];
+  __shared__ u32x4 xs_l[kDecodeMaxT * 4096 / 8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kb = lane >> 4;
   const int T = a.T, k = a.k, P = T * k, H = a.H, I = a.I;
-  decode_route(a, r);
-
   const PackGeom geom = pack_geom(I, H, 1);
   const int slot = blockIdx.x / geom.n_wt, wt = blockIdx.x % geom.n_wt;
+  const int G = geom.G;
+  constexpr int gpw = GPW;  // groups per wave (G <= kDecWaves * GPW)
+
+  // activations -> LDS (16 bytes per thread per pass)
+  const int n16 = T * H / 8;
+  for (int i = tid; i < n16; i += kDecThreads) xs_l[i] = reinterpret_cast<const u32x4*>(a.x)[i];
+
+  decode_route(a, r);
 
   if (blockIdx.x == 0) {
     if (tid < P) {
@@ -211,59 +328,51 @@ __global__ __launch_bounds__(512) void decode_gateup_kernel(DecodeArgs a) {
     if (slot >= r.n_uniq) return;
     expert = r.uniq[slot];
   }
-  // tokens of this block: token t uses slot jslot[t] (or -1)
   int jslot[kDecodeMaxT];
-  for (int t = 0; t < kDecodeMaxT; ++t) {
-    jslot[t] = -1;
-    if (t < T) {
-      if (expert < 0) {
-        jslot[t] = k;  // shared
-      } else {
-        for (int j = 0; j < k; ++j)
-          if (r.sel_e[t][j] == expert) jslot[t] = j;
-      }
-    }
-  }
+  token_slots(r, expert, T, k, jslot);
   const uint8_t* ebase = expert >= 0 ? a.gu_blob + (int64_t)expert * a.gu_expert_bytes : a.gu_shared;
-  const int G = geom.G;
-  const int gpw = (G + kDecWaves - 1) / kDecWaves;
-  float acc[4][kDecodeMaxT];
-  for (int ct = 0; ct < 4; ++ct)
-    for (int t = 0; t < kDecodeMaxT; ++t) acc[ct][t] = 0.f;
-  for (int gi = 0; gi < gpw; ++gi) {
+
+  // all weight loads of this wave's groups first
+  u32x4 w0[GPW], w1[GPW], sb[GPW];
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
     const int g = wave * gpw + gi;
-    if (g >= G) break;
-    const uint8_t* nib = ebase + geom.nib_off + (((int64_t)wt * G + g) * 128 + lane) * 16;
-    const u32x4 w0 = *reinterpret_cast<const u32x4*>(nib);
-    const u32x4 w1 = *reinterpret_cast<const u32x4*>(nib + 1024);
-    const u32x4 sbv = *reinterpret_cast<const u32x4*>(
-        ebase + geom.sb_off + (((int64_t)wt * G + g) * 16 + c16) * 16);
-    const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    const float s[4] = {bf16lo(sbv.x), bf16hi(sbv.x), bf16lo(sbv.y), bf16hi(sbv.y)};
-    const float b[4] = {bf16lo(sbv.z), bf16hi(sbv.z), bf16lo(sbv.w), bf16hi(sbv.w)};
-    for (int t = 0; t < T; ++t) {
-      if (jslot[t] < 0) continue;
-      const uint16_t* xr = a.x + (int64_t)t * H + g * kGroup + 8 * kb;
-      const u32x4 v0 = *reinterpret_cast<const u32x4*>(xr);
-      const u32x4 v1 = *reinterpret_cast<const u32x4*>(xr + 32);
-      const float x0[8] = {bf16lo(v0.x), bf16hi(v0.x), bf16lo(v0.y), bf16hi(v0.y),
-                           bf16lo(v0.z), bf16hi(v0.z), bf16lo(v0.w), bf16hi(v0.w)};
-      const float x1[8] = {bf16lo(v1.x), bf16hi(v1.x), bf16lo(v1.y), bf16hi(v1.y),
-                           bf16lo(v1.z), bf16hi(v1.z), bf16lo(v1.w), bf16hi(v1.w)};
-      float xsum = 0.f;
-      for (int o = 0; o < 8; ++o) xsum += x0[o] + x1[o];
-      for (int ct = 0; ct < 4; ++ct) {
-        const float pq = dot_codes(words[2 * ct], x0) + dot_codes(words[2 * ct + 1], x1);
-        acc[ct][t] += s[ct] * pq + b[ct] * xsum;
+    if (g < G) {
+      const uint8_t* nib = ebase + geom.nib_off + (((int64_t)wt * G + g) * 128 + lane) * 16;
+      w0[gi] = *reinterpret_cast<const u32x4*>(nib);
+      w1[gi] = *reinterpret_cast<const u32x4*>(nib + 1024);
+      sb[gi] = *reinterpret_cast<const u32x4*>(ebase + geom.sb_off + (((int64_t)wt * G + g) * 16 + c16) * 16);
+    }
+  }
+  const ExpandConsts xk = expand_consts();
+  float acc[kDecodeMaxT][4];
+#pragma unroll
+  for (int t = 0; t < kDecodeMaxT; ++t)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[t][ct] = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int g = wave * gpw + gi;
+    if (g < G) {
+#pragma unroll
+      for (int t = 0; t < kDecodeMaxT; ++t) {
+        if (t < T && jslot[t] >= 0) {
+          const int base16 = (t * H + g * kGroup + 8 * kb) / 8;
+          gemv_group(w0[gi], w1[gi], sb[gi], xs_l[base16], xs_l[base16 + 4], xk, acc[t]);
+        }
       }
     }
   }
-  for (int ct = 0; ct < 4; ++ct)
-    for (int t = 0; t < T; ++t) {
-      float v = acc[ct][t];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      if (kb == 0) red[wave][t][16 * ct + c16] = v;
+#pragma unroll
+  for (int t = 0; t < kDecodeMaxT; ++t)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      if (t < T) {
+        float v = acc[t][ct];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (kb == 0) red[wave][t][16 * ct + c16] = v;
+      }
     }
   __syncthreads();
   if (tid < T * 32) {
@@ -281,74 +390,70 @@ __global__ __launch_bounds__(512) void decode_gateup_kernel(DecodeArgs a) {
   }
 }
 
-// Grid: (k*T + 1) slots x (H/64) wave tiles; block: 512 threads (8 waves split K).
-__global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
+// Grid: (k*T + 1) slots x (H/64) wave tiles; block: 8 waves that split K.
+template <int GPW>
+__global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs a) {
   __shared__ DecodeRoute r;
   __shared__ float red[kDecWaves][kDecodeMaxT][kWaveCols];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kb = lane >> 4;
   const int T = a.T, k = a.k, P = T * k, H = a.H, I = a.I;
-  decode_route(a, r);
   const PackGeom geom = pack_geom(H, I, 0);
   const int slot = blockIdx.x / geom.n_wt, wt = blockIdx.x % geom.n_wt;
+  const int G = geom.G;
+  constexpr int gpw = GPW;  // groups per wave (G <= kDecWaves * GPW)
+  decode_route(a, r);
   int expert = -1;
   if (slot < P) {
     if (slot >= r.n_uniq) return;
     expert = r.uniq[slot];
   }
   int jslot[kDecodeMaxT];
-  for (int t = 0; t < kDecodeMaxT; ++t) {
-    jslot[t] = -1;
-    if (t < T) {
-      if (expert < 0) {
-        jslot[t] = k;
-      } else {
-        for (int j = 0; j < k; ++j)
-          if (r.sel_e[t][j] == expert) jslot[t] = j;
-      }
-    }
-  }
+  token_slots(r, expert, T, k, jslot);
   const uint8_t* ebase = expert >= 0 ? a.dn_blob + (int64_t)expert * a.dn_expert_bytes : a.dn_shared;
-  const int G = geom.G;
-  const int gpw = (G + kDecWaves - 1) / kDecWaves;
-  float acc[4][kDecodeMaxT];
-  for (int ct = 0; ct < 4; ++ct)
-    for (int t = 0; t < kDecodeMaxT; ++t) acc[ct][t] = 0.f;
-  for (int gi = 0; gi < gpw; ++gi) {
+
+  u32x4 w0[GPW], w1[GPW], sb[GPW];
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
     const int g = wave * gpw + gi;
-    if (g >= G) break;
-    const uint8_t* nib = ebase + geom.nib_off + (((int64_t)wt * G + g) * 128 + lane) * 16;
-    const u32x4 w0 = *reinterpret_cast<const u32x4*>(nib);
-    const u32x4 w1 = *reinterpret_cast<const u32x4*>(nib + 1024);
-    const u32x4 sbv = *reinterpret_cast<const u32x4*>(
-        ebase + geom.sb_off + (((int64_t)wt * G + g) * 16 + c16) * 16);
-    const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    const float s[4] = {bf16lo(sbv.x), bf16hi(sbv.x), bf16lo(sbv.y), bf16hi(sbv.y)};
-    const float b[4] = {bf16lo(sbv.z), bf16hi(sbv.z), bf16lo(sbv.w), bf16hi(sbv.w)};
-    for (int t = 0; t < T; ++t) {
-      if (jslot[t] < 0) continue;
-      const int row = jslot[t] == k ? k * T + t : t * k + jslot[t];
-      const uint16_t* hr = a.h + (int64_t)row * I + g * kGroup + 8 * kb;
-      const u32x4 h0 = *reinterpret_cast<const u32x4*>(hr);
-      const u32x4 h1 = *reinterpret_cast<const u32x4*>(hr + 32);
-      const float x0[8] = {bf16lo(h0.x), bf16hi(h0.x), bf16lo(h0.y), bf16hi(h0.y),
-                           bf16lo(h0.z), bf16hi(h0.z), bf16lo(h0.w), bf16hi(h0.w)};
-      const float x1[8] = {bf16lo(h1.x), bf16hi(h1.x), bf16lo(h1.y), bf16hi(h1.y),
-                           bf16lo(h1.z), bf16hi(h1.z), bf16lo(h1.w), bf16hi(h1.w)};
-      float xsum = 0.f;
-      for (int o = 0; o < 8; ++o) xsum += x0[o] + x1[o];
-      for (int ct = 0; ct < 4; ++ct) {
-        const float pq = dot_codes(words[2 * ct], x0) + dot_codes(words[2 * ct + 1], x1);
-        acc[ct][t] += s[ct] * pq + b[ct] * xsum;
+    if (g < G) {
+      const uint8_t* nib = ebase + geom.nib_off + (((int64_t)wt * G + g) * 128 + lane) * 16;
+      w0[gi] = *reinterpret_cast<const u32x4*>(nib);
+      w1[gi] = *reinterpret_cast<const u32x4*>(nib + 1024);
+      sb[gi] = *reinterpret_cast<const u32x4*>(ebase + geom.sb_off + (((int64_t)wt * G + g) * 16 + c16) * 16);
+    }
+  }
+  const ExpandConsts xk = expand_consts();
+  float acc[kDecodeMaxT][4];
+#pragma unroll
+  for (int t = 0; t < kDecodeMaxT; ++t)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[t][ct] = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int g = wave * gpw + gi;
+    if (g < G) {
+#pragma unroll
+      for (int t = 0; t < kDecodeMaxT; ++t) {
+        if (t < T && jslot[t] >= 0) {
+          const int row = jslot[t] == k ? k * T + t : t * k + jslot[t];
+          const uint16_t* hr = a.h + (int64_t)row * I + g * kGroup + 8 * kb;
+          gemv_group(w0[gi], w1[gi], sb[gi], *reinterpret_cast<const u32x4*>(hr),
+                     *reinterpret_cast<const u32x4*>(hr + 32), xk, acc[t]);
+        }
       }
     }
   }
-  for (int ct = 0; ct < 4; ++ct)
-    for (int t = 0; t < T; ++t) {
-      float v = acc[ct][t];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      if (kb == 0) red[wave][t][16 * ct + c16] = v;
+#pragma unroll
+  for (int t = 0; t < kDecodeMaxT; ++t)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      if (t < T) {
+        float v = acc[t][ct];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (kb == 0) red[wave][t][16 * ct + c16] = v;
+      }
     }
   __syncthreads();
   if (tid < T * kWaveCols) {
@@ -361,17 +466,47 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   }
 }
 
+namespace {
+
+// Smallest groups-per-wave instantiation that covers G groups with 8 waves.
+template <template <int> class KernelSel>
+hipError_t launch_gpw(int G, dim3 grid, hipStream_t s, const DecodeArgs& a) {
+  if (G <= kDecWaves)
+    hipLaunchKernelGGL(KernelSel<1>::fn(), grid, dim3(kDecThreads), 0, s, a);
+  else if (G <= 2 * kDecWaves)
+    hipLaunchKernelGGL(KernelSel<2>::fn(), grid, dim3(kDecThreads), 0, s, a);
+  else if (G <= 4 * kDecWaves)
+    hipLaunchKernelGGL(KernelSel<4>::fn(), grid, dim3(kDecThreads), 0, s, a);
+  else if (G <= 8 * kDecWaves)
+    hipLaunchKernelGGL(KernelSel<8>::fn(), grid, dim3(kDecThreads), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+template <int GPW>
+struct GateUpSel {
+  static auto fn() { return decode_gateup_kernel<GPW>; }
+};
+template <int GPW>
+struct DownSel {
+  static auto fn() { return decode_down_kernel<GPW>; }
+};
+
+}  // namespace
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
   const PackGeom gu = pack_geom(a.I, a.H, 1);
   const PackGeom dn = pack_geom(a.H, a.I, 0);
+  if (gu.G > kMaxGroups || dn.G > kMaxGroups || a.T > kDecodeMaxT) return hipErrorInvalidValue;
   const int slots = a.k * a.T + 1;
   hipError_t e = hipSuccess;
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_router_kernel, dim3((a.E + 3) / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(decode_router_kernel, dim3(a.E), dim3(256), 0, s, a);
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_gateup_kernel, dim3(slots * gu.n_wt), dim3(512), 0, s, a);
+  if ((e = launch_gpw<GateUpSel>(gu.G, dim3(slots * gu.n_wt), s, a)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_down_kernel, dim3(slots * dn.n_wt), dim3(512), 0, s, a);
+  if ((e = launch_gpw<DownSel>(dn.G, dim3(slots * dn.n_wt), s, a)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return e;
   if ((e = launch_combine(a.partial, a.topk_w, a.y, a.T, a.H, a.k, s)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[4], s)) != hipSuccess) return e;
