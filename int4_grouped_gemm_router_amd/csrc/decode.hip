@@ -21,6 +21,7 @@
 //   combine         y = bf16(shared + sum over the token's k slots), the same
 //                   kernel as the prefill path
 #include "kernels.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -36,77 +37,6 @@ __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
                                          false);
 }
 
-// Order-preserving u32 key of an fp32 logit: NaN counts as -inf and -0 as +0,
-// so equal keys are exactly equal logits (ties then go to the lower index).
-__device__ inline uint32_t logit_key(float v) {
-  v = v == v ? v : -INFINITY;
-  if (v == 0.f) v = 0.f;
-  const uint32_t u = __float_as_uint(v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Top-k (k <= 8) of one token's E <= 256 logits in one wave, in rank order
-// (logit descending, index ascending): lane j < k gets the j-th expert and
-// its logit. The k-th largest key is found bit by bit (a count of the keys at
-// or above each candidate per bit), then the selected keys are ranked.
-// `scratch` is this wave's 16-entry LDS area.
-__device__ void wave_topk(const float* __restrict__ row, int E, int k, int lane, uint32_t* scratch,
-                          int& sel_e, float& sel_l) {
-  const int per = E / 64;
-  uint32_t key[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) key[i] = i < per ? logit_key(row[lane + 64 * i]) : 0u;
-  uint32_t t = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t c = t | (1u << b);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(key[i] >= c));
-    if (cnt >= k) t = c;
-  }
-  // keys above t all belong to the top k; equal keys fill up by index
-  int need = k;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) need -= __popcll(__ballot(key[i] > t));
-  int base = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint64_t eqm = __ballot(key[i] == t);
-    const int before = __popcll(eqm & lanemask_lt());
-    const bool sel = key[i] > t || (key[i] == t && before < need);
-    const int taken = min(need, __popcll(eqm));
-    need -= taken;
-    const uint64_t sm = __ballot(sel);
-    if (sel) {
-      const int pos = base + __popcll(sm & lanemask_lt());
-      scratch[pos] = key[i];
-      scratch[8 + pos] = (uint32_t)(lane + 64 * i);
-    }
-    base += __popcll(sm);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  uint32_t my_key = 0, my_e = 0;
-  int rank = 0;
-  if (lane < k) {
-    my_key = scratch[lane];
-    my_e = scratch[8 + lane];
-    for (int m = 0; m < k; ++m) {
-      const uint32_t km = scratch[m], em = scratch[8 + m];
-      rank += (km > my_key) || (km == my_key && em < my_e);
-    }
-  }
-  // lane j < k takes the entry of rank j
-  int src = 0;
-  for (int m = 0; m < k; ++m) {
-    const int rm = __shfl(rank, m);
-    if (rm == lane) src = m;
-  }
-  sel_e = (int)__shfl((int)my_e, src);
-  sel_l = row[sel_e < E ? sel_e : 0];
-}
-
 // Routing state every decode block needs, rebuilt from the logits.
 struct DecodeRoute {
   int sel_e[kDecodeMaxT][8];
@@ -116,7 +46,7 @@ struct DecodeRoute {
   int uniq[kDecodeMaxT * 8];
   int uniq_first[kDecodeMaxT * 8];  // first sorted position of each unique expert
   int n_uniq;
-  uint32_t scratch[kDecodeMaxT][16];
+  uint32_t scratch[kDecodeMaxT][24];
 };
 
 // Requires kDecThreads threads; every thread must call it.
@@ -125,9 +55,18 @@ __device__ void decode_route(const DecodeArgs& a, DecodeRoute& r) {
   const int E = a.E, k = a.k, P = a.T * k;
   if (wave < a.T) {
     const int t = wave;
+    const float* row = a.logits + (int64_t)t * E;
+    uint32_t key[4];
+    float val[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = i < E / 64 ? row[lane + 64 * i] : -INFINITY;
+      val[i] = v == v ? v : -INFINITY;  // a NaN logit ranks as -inf
+      key[i] = i < E / 64 ? logit_key(val[i]) : 0u;
+    }
     int sel;
     float sel_l;
-    wave_topk(a.logits + (int64_t)t * E, E, k, lane, r.scratch[t], sel, sel_l);
+    wave_topk(key, val, k, lane, r.scratch[t], sel, sel_l);
     const float top = __shfl(sel_l, 0);
     const float p = lane < k ? expf(sel_l - top) : 0.f;
     const float z = wave_sum(p);

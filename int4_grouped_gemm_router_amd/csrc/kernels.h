@@ -14,7 +14,7 @@ constexpr int kChunkPairs = 1024;  // (token, slot) pairs per scatter block
 constexpr int kItemRows = 32;      // rows of one expert per GEMM work item (one routing block)
 constexpr int kMaxGroups = 64;     // K / 64 upper bound of the expert GEMMs
 constexpr int kDecodeMaxT = 4;
-constexpr int kMaxSplits = 4;      // router K splits summed by the top-k kernel
+constexpr int kMaxSplits = 8;      // router K splits summed by the top-k kernel
 
 struct TopkArgs {
   const float* partial;   // [splits][T][E]

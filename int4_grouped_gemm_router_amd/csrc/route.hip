@@ -18,6 +18,7 @@
 //                 (wave ballot peer matching), and, in block 0, the histogram,
 //                 offsets, the 32-row block map and the GEMM work list.
 #include "kernels.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -108,6 +109,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
 
 // Grid: ceil(T/4); one wave per token.
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
+  __shared__ uint32_t scratch[4][24];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= a.T) return;
@@ -131,38 +133,17 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
       for (int sp = 0; sp < kMaxSplits; ++sp) v += pv[sp][i];
       if (a.rbias) v += a.rbias[e];
       if (a.logits_out) a.logits_out[(int64_t)t * E + e] = v;
-      l[i] = v == v ? v : -INFINITY;  // a NaN logit never wins; the selection stays valid
+      l[i] = v == v ? v : -INFINITY;  // a NaN logit ranks as -inf
     }
   }
-  // top-k by repeated wave argmax; (value desc, index asc)
-  uint32_t taken = 0;
-  int sel_e = -1;
-  float sel_l = 0.f, top = 0.f;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-    for (int i = 0; i < per; ++i) {
-      const int e = lane + 64 * i;
-      if (!((taken >> i) & 1u) && (l[i] > bv || (l[i] == bv && e < bi))) {
-        bv = l[i];
-        bi = e;
-      }
-    }
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (j == 0) top = bv;
-    if (lane == j) {
-      sel_e = bi;
-      sel_l = bv;
-    }
-  }
+  // top-k: value descending, index ascending
+  uint32_t key[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) key[i] = i < per ? logit_key(l[i]) : 0u;
+  int sel_e;
+  float sel_l;
+  wave_topk(key, l, k, lane, scratch[wave], sel_e, sel_l);
+  const float top = __shfl(sel_l, 0);
   // weights: exp(l_j - l_0) / sum over the k selected
   const float p = lane < k ? expf(sel_l - top) : 0.f;
   const float z = wave_sum(p);
