@@ -150,15 +150,15 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs a) {
   const int n_wt = geom.n_wt;
   const int n_tiles = (n_wt + kWaves - 1) / kWaves;
 
-  // Blocks are dispatched round-robin over the 8 XCDs; the blocks of XCD x
-  // take the units of slots x, x+8, ..., so the column tiles of one item run
-  // on one XCD at about the same time and share its gathered rows in L2.
+  // Blocks are dispatched round-robin over the 8 XCDs (block b on XCD b & 7).
   const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, nbx = gridDim.x >> 3;
   const int ni = *a.num_items;
   const int n_slots = ni + a.shared_slots;
-  const int slots_x = n_slots > xcd ? (n_slots - xcd + 7) >> 3 : 0;
-  const int units_x = slots_x * n_tiles;
-  const int my_units = units_x > lb ? (units_x - lb + nbx - 1) / nbx : 0;
+  // XCD x owns the contiguous unit range [u0, u1) (units are slot-major), so
+  // the column tiles of one item, and the items of one expert, share an L2
+  const int n_units = n_slots * n_tiles;
+  const int u0 = (int)((int64_t)n_units * xcd / 8), u1 = (int)((int64_t)n_units * (xcd + 1) / 8);
+  const int my_units = u1 - u0 > lb ? (u1 - u0 - lb + nbx - 1) / nbx : 0;
   const ExpandConsts xk = expand_consts();
 
   // lane roles in the copies
@@ -169,8 +169,8 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs a) {
     const int nb = min(kBatch, my_units - base);
     lds_barrier();  // the previous batch is done with the tables
     if (tid < nb) {
-      const int v = lb + (base + tid) * nbx;
-      const int slot = 8 * (v / n_tiles) + xcd;
+      const int v = u0 + lb + (base + tid) * nbx;
+      const int slot = v / n_tiles;
       UnitInfo u;
       u.nt = v % n_tiles;
       if (slot < ni) {
@@ -369,9 +369,11 @@ __global__ __launch_bounds__(kRThreads, 2) void gemm_ring_kernel(GemmArgs a) {
   const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, nbx = gridDim.x >> 3;
   const int ni = *a.num_items;
   const int n_slots = ni + a.shared_slots;
-  const int slots_x = n_slots > xcd ? (n_slots - xcd + 7) >> 3 : 0;
-  const int units_x = slots_x * n_tiles;
-  const int my_units = units_x > lb ? (units_x - lb + nbx - 1) / nbx : 0;
+  // XCD x owns the contiguous unit range [u0, u1) (units are slot-major), so
+  // the column tiles of one item, and the items of one expert, share an L2
+  const int n_units = n_slots * n_tiles;
+  const int u0 = (int)((int64_t)n_units * xcd / 8), u1 = (int)((int64_t)n_units * (xcd + 1) / 8);
+  const int my_units = u1 - u0 > lb ? (u1 - u0 - lb + nbx - 1) / nbx : 0;
   const ExpandConsts xk = expand_consts();
 
   const int xu = 64 * wave + lane;                                 // 16-byte unit of the x stage
@@ -381,8 +383,8 @@ __global__ __launch_bounds__(kRThreads, 2) void gemm_ring_kernel(GemmArgs a) {
     const int nb = min(kBatch, my_units - base);
     lds_barrier();
     if (tid < nb) {
-      const int v = lb + (base + tid) * nbx;
-      const int slot = 8 * (v / n_tiles) + xcd;
+      const int v = u0 + lb + (base + tid) * nbx;
+      const int slot = v / n_tiles;
       UnitInfo u;
       u.nt = v % n_tiles;
       if (slot < ni) {
