@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2516.6
 PREFILL_KERNELS = ["router", "topk", "scan_scatter", "gemm_gateup", "gemm_down", "combine"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gateup_prefill_t512.json")
-DECODE_KERNELS = ["decode_router", "decode_gateup", "decode_down", "decode_combine"]
+DECODE_KERNELS = ["decode_router", "decode_topk_gateup", "decode_down_combine"]
 
 
 def log(*a):
@@ -180,7 +180,8 @@ def run_decode(name, steps, warmup, copies):
         B.moe_decode_layer(d, dws[0], xd[warmup + i], y, T, None, ro, ws)
         hists.append(ro.hist.clone())
     # eager pass with events: per-kernel durations
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    nk = len(DECODE_KERNELS)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
     arrays = [B._event_array(ev) for ev in events]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -189,7 +190,7 @@ def run_decode(name, steps, warmup, copies):
     torch.cuda.synchronize()
     wall_eager = time.perf_counter() - t0
     y_eager = y.clone()
-    per = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(4)]
+    per = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(nk)]
                     for i in range(steps)])
     kern_ms = per.mean(axis=0)
     # timed region: one graph of all steps

@@ -167,9 +167,9 @@ int moe_decode_layer(const moe_dims* dims, const moe_layer_weights* w, const uin
  * handles created by the caller) on `stream`: events[i] just before the i-th
  * kernel launch and one more after the last launch, so consecutive events
  * bracket one kernel each. Prefill launches 6 kernels per chunk (router,
- * top-k, scan/scatter, gate/up, routed down, shared down + combine) and needs
- * n_events >= 6 * chunks + 1; decode launches 4 (router, gate/up, down,
- * combine) and needs n_events >= 5. MOE_EINVAL if too few events. */
+ * top-k, scan/scatter, gate/up, down, combine) and needs
+ * n_events >= 6 * chunks + 1; decode launches 3 (router, top-k + gate/up,
+ * down + combine) and needs n_events >= 4. MOE_EINVAL if too few events. */
 int moe_prefill_layer_profiled(const moe_dims* dims, const moe_layer_weights* w,
                                const uint16_t* x, uint16_t* y, int32_t T, int32_t chunk_T,
                                float* logits_out, const moe_route_out* route_out, void* ws,

@@ -84,7 +84,7 @@ PrefillWs carve_prefill(const moe_dims* d, int Tc, void* ws, size_t* bytes) {
 }
 
 struct DecodeWs {
-  float *logits, *topk_w, *partial;
+  float *logits, *topk_w;
   int32_t* topk_idx;
   uint16_t* h;
 };
@@ -97,7 +97,6 @@ DecodeWs carve_decode(const moe_dims* d, int T, void* ws, size_t* bytes) {
   w.topk_idx = c.take<int32_t>((size_t)k * T);
   w.topk_w = c.take<float>((size_t)k * T);
   w.h = c.take<uint16_t>((size_t)(k + 1) * T * d->I);
-  w.partial = c.take<float>((size_t)(k + 1) * T * d->H);
   *bytes = c.used;
   return w;
 }
@@ -128,7 +127,7 @@ struct Recorder {
 };
 
 constexpr int kPrefillLaunchesPerChunk = 6;
-constexpr int kDecodeLaunches = 4;
+constexpr int kDecodeLaunches = 3;
 
 int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x, uint16_t* y,
                  int32_t T, int32_t chunk_T, float* logits_out, const moe_route_out* route_out,
@@ -399,7 +398,6 @@ int decode_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_t
   a.dn_shared = static_cast<const uint8_t*>(w->shared_down) + kHeaderBytes;
   a.dn_expert_bytes = dn.expert_bytes;
   a.h = W.h;
-  a.partial = W.partial;
   a.y = y;
   a.T = T;
   a.H = dims->H;

@@ -3,23 +3,23 @@
 // diariobitcoin.com, "Perplexity libera Lily, un motor de IA que supera a
 // MLX-LM en Apple Silicon", section "El decode busca mover menos datos": at
 // batch 1 there is little weight reuse and memory bandwidth is the ceiling.
-// The pass therefore reads only the selected experts' packed weights, once
-// each (a token set that picks the same expert twice shares one read), with
+// The pass therefore reads only the selected experts' packed weights, with
 // coalesced 16-byte loads spread over many waves, each wave issuing all of
 // its loads at once; codes are expanded to exact bf16 (128 + q) and
 // multiplied by bf16 dot-product instructions with fp32 accumulation.
 //
-// Four launches on the caller's stream, no host synchronisation:
+// Three launches on the caller's stream, no host synchronisation:
 //   decode_router   fp32 router logits, one block per expert
-//   decode_gateup   top-k of every token (recomputed per block from the
-//                   logits), the unique selected experts in ascending order,
-//                   then gate/up + SwiGLU for (unique expert or shared expert)
-//                   x (64-column wave tile); block 0 also writes the routing
-//                   metadata
-//   decode_down     down projection per (expert, 64-row tile) into
-//                   per-(token, slot) fp32 rows
-//   combine         y = bf16(shared + sum over the token's k slots), the same
-//                   kernel as the prefill path
+//   decode_gateup   every block recomputes the top-k of every token from the
+//                   logits (one wave per token) and the ascending list of
+//                   unique selected experts, then computes gate/up + SwiGLU
+//                   for (unique expert or shared expert) x (64-column wave
+//                   tile); a token set that picks one expert twice shares its
+//                   read; block 0 also writes the routing metadata
+//   decode_down     per 64-column tile of the output: the down projection of
+//                   every (token, slot) pair, then
+//                   y = bf16(shared + sum over the token's k slots of
+//                   weight * output) in a fixed order
 #include "kernels.h"
 #include "topk.h"
 
@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kK = 8;  // experts per token
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -38,21 +39,21 @@ __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 // Routing state every decode block needs, rebuilt from the logits.
+// Pairs are (token t, rank j) -> index t * kK + j.
 struct DecodeRoute {
-  int sel_e[kDecodeMaxT][8];
-  float sel_w[kDecodeMaxT][8];
-  int sorted_pair[kDecodeMaxT * 8];
-  int pos_of_pair[kDecodeMaxT * 8];
-  int uniq[kDecodeMaxT * 8];
-  int uniq_first[kDecodeMaxT * 8];  // first sorted position of each unique expert
+  int sel_e[kDecodeMaxT * kK];
+  float sel_w[kDecodeMaxT * kK];
+  int sorted_pair[kDecodeMaxT * kK];
+  int pos_of_pair[kDecodeMaxT * kK];
+  int uniq[kDecodeMaxT * kK];
+  int uniq_first[kDecodeMaxT * kK];  // first sorted position of each unique expert
   int n_uniq;
-  uint32_t scratch[kDecodeMaxT][24];
 };
 
 // Requires kDecThreads threads; every thread must call it.
 __device__ void decode_route(const DecodeArgs& a, DecodeRoute& r) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = a.E, k = a.k, P = a.T * k;
+  const int E = a.E, P = a.T * kK;
   if (wave < a.T) {
     const int t = wave;
     const float* row = a.logits + (int64_t)t * E;
@@ -66,21 +67,21 @@ __device__ void decode_route(const DecodeArgs& a, DecodeRoute& r) {
     }
     int sel;
     float sel_l;
-    wave_topk(key, val, k, lane, r.scratch[t], sel, sel_l);
+    wave_topk(key, val, kK, lane, sel, sel_l);
     const float top = __shfl(sel_l, 0);
-    const float p = lane < k ? expf(sel_l - top) : 0.f;
+    const float p = lane < kK ? expf(sel_l - top) : 0.f;
     const float z = wave_sum(p);
-    if (lane < k) {
-      r.sel_e[t][lane] = sel;
-      r.sel_w[t][lane] = p / z;
+    if (lane < kK) {
+      r.sel_e[t * kK + lane] = sel;
+      r.sel_w[t * kK + lane] = p / z;
     }
   }
   __syncthreads();
   if (tid < P) {
-    const int e = r.sel_e[tid / k][tid % k];
+    const int e = r.sel_e[tid];
     int pos = 0;
     for (int q = 0; q < P; ++q) {
-      const int eq = r.sel_e[q / k][q % k];
+      const int eq = r.sel_e[q];
       pos += (eq < e) || (eq == e && q < tid);
     }
     r.sorted_pair[pos] = tid;
@@ -91,13 +92,8 @@ __device__ void decode_route(const DecodeArgs& a, DecodeRoute& r) {
     bool first = false;
     int e = -1;
     if (lane < P) {
-      const int q = r.sorted_pair[lane];
-      e = r.sel_e[q / k][q % k];
-      first = lane == 0;
-      if (lane > 0) {
-        const int q0 = r.sorted_pair[lane - 1];
-        first = r.sel_e[q0 / k][q0 % k] != e;
-      }
+      e = r.sel_e[r.sorted_pair[lane]];
+      first = lane == 0 || r.sel_e[r.sorted_pair[lane - 1]] != e;
     }
     const uint64_t fm = __ballot(first);
     if (first) {
@@ -110,39 +106,42 @@ __device__ void decode_route(const DecodeArgs& a, DecodeRoute& r) {
   __syncthreads();
 }
 
-// Slot of token t in this block's expert (k for the shared expert), or -1.
-__device__ inline void token_slots(const DecodeRoute& r, int expert, int T, int k, int (&jslot)[kDecodeMaxT]) {
+// Slot of token t in this block's expert (kK for the shared expert), or -1.
+__device__ inline void token_slots(const DecodeRoute& r, int expert, int T, int (&jslot)[kDecodeMaxT]) {
 #pragma unroll
   for (int t = 0; t < kDecodeMaxT; ++t) {
     jslot[t] = -1;
     if (t < T) {
       if (expert < 0) {
-        jslot[t] = k;
+        jslot[t] = kK;
       } else {
-        for (int j = 0; j < k; ++j)
-          if (r.sel_e[t][j] == expert) jslot[t] = j;
+#pragma unroll
+        for (int j = 0; j < kK; ++j)
+          if (r.sel_e[t * kK + j] == expert) jslot[t] = j;
       }
     }
   }
 }
 
-// Partial dot products of one lane for one group: the lane's 16 inputs of
-// the group (x0: k = 8kb.., x1: k = 32 + 8kb..) against its four columns'
-// codes; acc[ct] += s * sum(x (128 + q)) + (b - 128 s) * sum(x).
-__device__ inline void gemv_group(const u32x4 w0, const u32x4 w1, const u32x4 sbv, const u32x4 x0,
-                                  const u32x4 x1, const ExpandConsts xk, float (&acc)[4]) {
-  const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+// Partial dot products of one lane for one group and one half of a 64-column
+// wave tile (column tiles 2 half and 2 half + 1): the lane's 16 inputs of the
+// group (x0: k = 8kb.., x1: k = 32 + 8kb..) against its two columns' codes
+// (w: the half's 16 bytes); acc[c] += s * sum(x (128 + q)) + (b - 128 s) * sum(x).
+__device__ inline void gemv_half(const u32x4 w, const u32x4 sbv, int half, const u32x4 x0,
+                                 const u32x4 x1, const ExpandConsts xk, float (&acc)[2]) {
+  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
   const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-  const float sc[4] = {bf16lo(sbv.x), bf16hi(sbv.x), bf16lo(sbv.y), bf16hi(sbv.y)};
-  const float bi[4] = {bf16lo(sbv.z), bf16hi(sbv.z), bf16lo(sbv.w), bf16hi(sbv.w)};
+  const uint32_t s2 = half ? sbv.y : sbv.x, b2 = half ? sbv.w : sbv.z;
+  const float sc[2] = {bf16lo(s2), bf16hi(s2)};
+  const float bi[2] = {bf16lo(b2), bf16hi(b2)};
   constexpr uint32_t kOnes = 0x3F803F80u;
   float xsum = 0.f;
 #pragma unroll
   for (int d = 0; d < 8; ++d) xsum = dot2(xs[d], kOnes, xsum);
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const u32x4 b0 = expand_codes(words[2 * ct], xk);
-    const u32x4 b1 = expand_codes(words[2 * ct + 1], xk);
+  for (int c = 0; c < 2; ++c) {
+    const u32x4 b0 = expand_codes(words[2 * c], xk);
+    const u32x4 b1 = expand_codes(words[2 * c + 1], xk);
     float p = 0.f;
     p = dot2(b0.x, xs[0], p);
     p = dot2(b0.y, xs[1], p);
@@ -152,7 +151,7 @@ __device__ inline void gemv_group(const u32x4 w0, const u32x4 w1, const u32x4 sb
     p = dot2(b1.y, xs[5], p);
     p = dot2(b1.z, xs[6], p);
     p = dot2(b1.w, xs[7], p);
-    acc[ct] = __builtin_fmaf(bi[ct] - 128.0f * sc[ct], xsum, __builtin_fmaf(sc[ct], p, acc[ct]));
+    acc[c] = __builtin_fmaf(bi[c] - 128.0f * sc[c], xsum, __builtin_fmaf(sc[c], p, acc[c]));
   }
 }
 
@@ -204,44 +203,49 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
   }
 }
 
-// Grid: (k*T + 1) slots x n_wt wave tiles; block: 8 waves that split K.
-// Slot < k*T: the slot-th unique selected expert (blocks past the number of
-// unique experts exit); slot k*T: the shared expert. The tokens' activations
-// are staged in LDS while the block recomputes the routing; then each wave
-// issues all of its groups' weight loads at once.
+// Grid: (k*T + 1) slots x n_wt wave tiles x 2 halves; block: 8 waves that
+// split K. Slot < k*T: the slot-th unique selected expert (blocks past the
+// number of unique experts exit); slot k*T: the shared expert. A half of a
+// 64-column wave tile is 16 gate and the matching 16 up columns. The
+// activations are loaded before the routing is recomputed and staged in LDS
+// after it; then each wave issues all of its groups' weight loads at once.
 template <int GPW>
 __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a) {
   __shared__ DecodeRoute r;
-  __shared__ float red[kDecWaves][kDecodeMaxT][kWaveCols];
+  __shared__ float red[kDecWaves][kDecodeMaxT][kWaveCols / 2];
   __shared__ u32x4 xs_l[kDecodeMaxT * 4096 / 8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kb = lane >> 4;
-  const int T = a.T, k = a.k, P = T * k, H = a.H, I = a.I;
+  const int T = a.T, P = T * kK, H = a.H, I = a.I;
   const PackGeom geom = pack_geom(I, H, 1);
-  const int slot = blockIdx.x / geom.n_wt, wt = blockIdx.x % geom.n_wt;
+  const int half = blockIdx.x & 1;
+  const int slot = (blockIdx.x >> 1) / geom.n_wt, wt = (blockIdx.x >> 1) % geom.n_wt;
   const int G = geom.G;
   constexpr int gpw = GPW;  // groups per wave (G <= kDecWaves * GPW)
+  constexpr int kXPer = kDecodeMaxT * 4096 / 8 / kDecThreads;
 
-  // activations -> LDS (16 bytes per thread per pass)
   const int n16 = T * H / 8;
-  for (int i = tid; i < n16; i += kDecThreads) xs_l[i] = reinterpret_cast<const u32x4*>(a.x)[i];
+  u32x4 xv[kXPer];  // (clamped, unconditional loads: no branches between them)
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i)
+    xv[i] = reinterpret_cast<const u32x4*>(a.x)[min(tid + i * kDecThreads, n16 - 1)];
 
   decode_route(a, r);
 
   if (blockIdx.x == 0) {
     if (tid < P) {
-      a.topk_idx[tid] = r.sel_e[tid / k][tid % k];
-      a.topk_w[tid] = r.sel_w[tid / k][tid % k];
+      a.topk_idx[tid] = r.sel_e[tid];
+      a.topk_w[tid] = r.sel_w[tid];
       if (a.perm) {
         a.perm[r.pos_of_pair[tid]] = tid;
         a.inv_perm[tid] = r.pos_of_pair[tid];
       }
     }
     if (a.hist) {
-      for (int e = tid; e < a.E; e += blockDim.x) {
+      for (int e = tid; e < a.E; e += kDecThreads) {
         int c = 0, off = 0;
         for (int q = 0; q < P; ++q) {
-          const int eq = r.sel_e[q / k][q % k];
+          const int eq = r.sel_e[q];
           c += eq == e;
           off += eq < e;
         }
@@ -268,27 +272,30 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
     expert = r.uniq[slot];
   }
   int jslot[kDecodeMaxT];
-  token_slots(r, expert, T, k, jslot);
+  token_slots(r, expert, T, jslot);
   const uint8_t* ebase = expert >= 0 ? a.gu_blob + (int64_t)expert * a.gu_expert_bytes : a.gu_shared;
 
-  // all weight loads of this wave's groups first
-  u32x4 w0[GPW], w1[GPW], sb[GPW];
+  // (unconditional loads, groups past G clamped to G - 1 and not used: no
+  // branches between the loads)
+  u32x4 wq[GPW], sb[GPW];
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
-    const int g = wave * gpw + gi;
-    if (g < G) {
-      const uint8_t* nib = ebase + geom.nib_off + (((int64_t)wt * G + g) * 128 + lane) * 16;
-      w0[gi] = *reinterpret_cast<const u32x4*>(nib);
-      w1[gi] = *reinterpret_cast<const u32x4*>(nib + 1024);
-      sb[gi] = *reinterpret_cast<const u32x4*>(ebase + geom.sb_off + (((int64_t)wt * G + g) * 16 + c16) * 16);
-    }
+    const int g = min(wave * gpw + gi, G - 1);
+    wq[gi] = *reinterpret_cast<const u32x4*>(ebase + geom.nib_off +
+                                             (((int64_t)wt * G + g) * 128 + 64 * half + lane) * 16);
+    sb[gi] = *reinterpret_cast<const u32x4*>(ebase + geom.sb_off + (((int64_t)wt * G + g) * 16 + c16) * 16);
   }
+  // keep every weight load ahead of the arithmetic (one memory round trip)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i)
+    if (tid + i * kDecThreads < n16) xs_l[tid + i * kDecThreads] = xv[i];
+  __syncthreads();
+
   const ExpandConsts xk = expand_consts();
-  float acc[kDecodeMaxT][4];
+  float acc[kDecodeMaxT][2];
 #pragma unroll
-  for (int t = 0; t < kDecodeMaxT; ++t)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[t][ct] = 0.f;
+  for (int t = 0; t < kDecodeMaxT; ++t) acc[t][0] = acc[t][1] = 0.f;
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     const int g = wave * gpw + gi;
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
       for (int t = 0; t < kDecodeMaxT; ++t) {
         if (t < T && jslot[t] >= 0) {
           const int base16 = (t * H + g * kGroup + 8 * kb) / 8;
-          gemv_group(w0[gi], w1[gi], sb[gi], xs_l[base16], xs_l[base16 + 4], xk, acc[t]);
+          gemv_half(wq[gi], sb[gi], half, xs_l[base16], xs_l[base16 + 4], xk, acc[t]);
         }
       }
     }
@@ -305,150 +312,168 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
 #pragma unroll
   for (int t = 0; t < kDecodeMaxT; ++t)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int c = 0; c < 2; ++c) {
       if (t < T) {
-        float v = acc[t][ct];
+        float v = acc[t][c];
         v += __shfl_xor(v, 16);
         v += __shfl_xor(v, 32);
-        if (kb == 0) red[wave][t][16 * ct + c16] = v;
+        if (kb == 0) red[wave][t][16 * c + c16] = v;  // c = 0: gate, c = 1: up
       }
     }
   __syncthreads();
-  if (tid < T * 32) {
-    const int t = tid / 32, j = tid % 32;
+  if (tid < T * 16) {
+    const int t = tid / 16, j = tid % 16;
     if (jslot[t] >= 0) {
       float gv = 0.f, uv = 0.f;
-      const int jg = 32 * (j >> 4) + (j & 15);  // gate column of intermediate j; up is 16 later
       for (int w = 0; w < kDecWaves; ++w) {
-        gv += red[w][t][jg];
-        uv += red[w][t][jg + 16];
+        gv += red[w][t][j];
+        uv += red[w][t][16 + j];
       }
-      const int row = jslot[t] == k ? k * T + t : t * k + jslot[t];
-      a.h[(int64_t)row * I + 32 * wt + j] = f2bf(silu(gv) * uv);
+      const int row = jslot[t] == kK ? kK * T + t : t * kK + jslot[t];
+      a.h[(int64_t)row * I + 32 * wt + 16 * half + j] = f2bf(silu(gv) * uv);
     }
   }
 }
 
-// Grid: (k*T + 1) slots x (H/64) wave tiles; block: 8 waves that split K.
-template <int GPW>
+// Down projection and combine. Grid: H/64 column tiles x 2 halves of 32
+// columns; block: 8 waves.
+// Work is (token t, slot j) pairs, p = t (k+1) + j, slot k being the shared
+// expert, nine pairs at a time. Per batch of pairs and round of eight groups,
+// wave w takes group w of the round: the pairs' expert ids, then all their
+// weight loads and, at the same time, the block's copy of the pairs'
+// activation rows into LDS, one barrier, and the arithmetic; the column sums
+// of each pair stay in registers over the rounds. Then per pair
+// d[t][j] = sum over the eight waves in order, and
+// y[t] = bf16(d[t][k] + sum_{j<k} w[t][j] * d[t][j]), j ascending.
+constexpr int kDecPairs = kDecodeMaxT * (kK + 1);
+constexpr int kDecPairBatch = kK + 1;
+
 __global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs a) {
-  __shared__ DecodeRoute r;
-  __shared__ float red[kDecWaves][kDecodeMaxT][kWaveCols];
+  __shared__ float red[kDecWaves][kDecPairs][kWaveCols / 2];
+  __shared__ u32x4 hs[kDecPairBatch][kDecWaves * kGroup / 8];  // [pair][group in round][8 inputs]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kb = lane >> 4;
-  const int T = a.T, k = a.k, P = T * k, H = a.H, I = a.I;
+  const int T = a.T, H = a.H, I = a.I;
   const PackGeom geom = pack_geom(H, I, 0);
-  const int slot = blockIdx.x / geom.n_wt, wt = blockIdx.x % geom.n_wt;
-  const int G = geom.G;
-  constexpr int gpw = GPW;  // groups per wave (G <= kDecWaves * GPW)
-  decode_route(a, r);
-  int expert = -1;
-  if (slot < P) {
-    if (slot >= r.n_uniq) return;
-    expert = r.uniq[slot];
-  }
-  int jslot[kDecodeMaxT];
-  token_slots(r, expert, T, k, jslot);
-  const uint8_t* ebase = expert >= 0 ? a.dn_blob + (int64_t)expert * a.dn_expert_bytes : a.dn_shared;
-
-  u32x4 w0[GPW], w1[GPW], sb[GPW];
-#pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
-    const int g = wave * gpw + gi;
-    if (g < G) {
-      const uint8_t* nib = ebase + geom.nib_off + (((int64_t)wt * G + g) * 128 + lane) * 16;
-      w0[gi] = *reinterpret_cast<const u32x4*>(nib);
-      w1[gi] = *reinterpret_cast<const u32x4*>(nib + 1024);
-      sb[gi] = *reinterpret_cast<const u32x4*>(ebase + geom.sb_off + (((int64_t)wt * G + g) * 16 + c16) * 16);
-    }
-  }
+  const int wt = blockIdx.x >> 1, half = blockIdx.x & 1, G = geom.G;
+  const int n_pairs = (kK + 1) * T;
   const ExpandConsts xk = expand_consts();
-  float acc[kDecodeMaxT][4];
+  for (int p0 = 0; p0 < n_pairs; p0 += kDecPairBatch) {
+    const int nb = min(kDecPairBatch, n_pairs - p0);
+    int ex[kDecPairBatch];
 #pragma unroll
-  for (int t = 0; t < kDecodeMaxT; ++t)
+    for (int b = 0; b < kDecPairBatch; ++b) {
+      const int p = min(p0 + b, n_pairs - 1), t = p / (kK + 1), j = p % (kK + 1);
+      ex[b] = j < kK ? a.topk_idx[t * kK + j] : -1;  // -1: the shared expert
+    }
+    float acc[kDecPairBatch][2];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[t][ct] = 0.f;
+    for (int b = 0; b < kDecPairBatch; ++b) acc[b][0] = acc[b][1] = 0.f;
+    for (int r0 = 0; r0 < G; r0 += kDecWaves) {
+      const int ng = min(kDecWaves, G - r0), g = r0 + wave;
+      static_assert(kDecWaves * kGroup / 8 == 64, "LDS row of the round: 64 chunks of 8 inputs");
+      // activation rows of this batch and round (independent of the expert ids)
+      constexpr int kHsPer = (kDecPairBatch * kDecWaves * kGroup / 8 + kDecThreads - 1) / kDecThreads;
+      // (unconditional, clamped loads: no branches between the loads)
+      u32x4 hv[kHsPer];
 #pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
-    const int g = wave * gpw + gi;
-    if (g < G) {
+      for (int q = 0; q < kHsPer; ++q) {
+        const int i = tid + q * kDecThreads;
+        const int b = min(i >> 6, nb - 1), c = min(i & 63, 8 * ng - 1), p = p0 + b;
+        const int t = p / (kK + 1), j = p % (kK + 1);
+        const int row = j < kK ? t * kK + j : kK * T + t;
+        hv[q] = *reinterpret_cast<const u32x4*>(a.h + (int64_t)row * I + r0 * kGroup + 8 * c);
+      }
+      u32x4 wq[kDecPairBatch], sb[kDecPairBatch];
+      const int gl = min(g, G - 1);  // waves past G load group G - 1 and do not use it
 #pragma unroll
-      for (int t = 0; t < kDecodeMaxT; ++t) {
-        if (t < T && jslot[t] >= 0) {
-          const int row = jslot[t] == k ? k * T + t : t * k + jslot[t];
-          const uint16_t* hr = a.h + (int64_t)row * I + g * kGroup + 8 * kb;
-          gemv_group(w0[gi], w1[gi], sb[gi], *reinterpret_cast<const u32x4*>(hr),
-                     *reinterpret_cast<const u32x4*>(hr + 32), xk, acc[t]);
+      for (int b = 0; b < kDecPairBatch; ++b) {
+        const int e = __builtin_amdgcn_readfirstlane(ex[b]);
+        const uint8_t* eb = e >= 0 ? a.dn_blob + (int64_t)e * a.dn_expert_bytes : a.dn_shared;
+        wq[b] = *reinterpret_cast<const u32x4*>(eb + geom.nib_off +
+                                                (((int64_t)wt * G + gl) * 128 + 64 * half + lane) * 16);
+        sb[b] = *reinterpret_cast<const u32x4*>(eb + geom.sb_off + (((int64_t)wt * G + gl) * 16 + c16) * 16);
+      }
+      // keep every load of the batch ahead of the LDS copy and the arithmetic
+      __builtin_amdgcn_sched_barrier(0);
+      if (p0 > 0 || r0 > 0) __syncthreads();  // every wave is done with the previous rows
+#pragma unroll
+      for (int q = 0; q < kHsPer; ++q) {
+        const int i = tid + q * kDecThreads;
+        if ((i >> 6) < nb && (i & 63) < 8 * ng) hs[i >> 6][i & 63] = hv[q];
+      }
+      __syncthreads();
+      if (g < G) {
+        const int c = 8 * wave + kb;
+#pragma unroll
+        for (int b = 0; b < kDecPairBatch; ++b)
+          if (b < nb) gemv_half(wq[b], sb[b], half, hs[b][c], hs[b][c + 4], xk, acc[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kDecPairBatch; ++b) {
+      if (b < nb) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          float v = acc[b][c];
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 32);
+          if (kb == 0) red[wave][p0 + b][16 * c + c16] = v;
         }
       }
     }
   }
-#pragma unroll
-  for (int t = 0; t < kDecodeMaxT; ++t)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      if (t < T) {
-        float v = acc[t][ct];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        if (kb == 0) red[wave][t][16 * ct + c16] = v;
-      }
-    }
   __syncthreads();
-  if (tid < T * kWaveCols) {
-    const int t = tid / kWaveCols, j = tid % kWaveCols;
-    if (jslot[t] >= 0) {
-      float d = 0.f;
-      for (int w = 0; w < kDecWaves; ++w) d += red[w][t][j];
-      a.partial[((int64_t)t * (k + 1) + jslot[t]) * H + 64 * wt + j] = d;
+  if (tid < T * kWaveCols / 2) {
+    const int t = tid / (kWaveCols / 2), n = tid % (kWaveCols / 2);
+    float d[kK + 1];
+#pragma unroll
+    for (int j = 0; j <= kK; ++j) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) v += red[w][t * (kK + 1) + j][n];
+      d[j] = v;
     }
+    float s = d[kK];
+#pragma unroll
+    for (int j = 0; j < kK; ++j) s = __builtin_fmaf(a.topk_w[t * kK + j], d[j], s);
+    a.y[(int64_t)t * H + 64 * wt + 32 * half + n] = f2bf(s);
   }
 }
 
 namespace {
 
 // Smallest groups-per-wave instantiation that covers G groups with 8 waves.
-template <template <int> class KernelSel>
-hipError_t launch_gpw(int G, dim3 grid, hipStream_t s, const DecodeArgs& a) {
+hipError_t launch_gateup(int G, dim3 grid, hipStream_t s, const DecodeArgs& a) {
   if (G <= kDecWaves)
-    hipLaunchKernelGGL(KernelSel<1>::fn(), grid, dim3(kDecThreads), 0, s, a);
+    hipLaunchKernelGGL(decode_gateup_kernel<1>, grid, dim3(kDecThreads), 0, s, a);
   else if (G <= 2 * kDecWaves)
-    hipLaunchKernelGGL(KernelSel<2>::fn(), grid, dim3(kDecThreads), 0, s, a);
+    hipLaunchKernelGGL(decode_gateup_kernel<2>, grid, dim3(kDecThreads), 0, s, a);
   else if (G <= 4 * kDecWaves)
-    hipLaunchKernelGGL(KernelSel<4>::fn(), grid, dim3(kDecThreads), 0, s, a);
+    hipLaunchKernelGGL(decode_gateup_kernel<4>, grid, dim3(kDecThreads), 0, s, a);
   else if (G <= 8 * kDecWaves)
-    hipLaunchKernelGGL(KernelSel<8>::fn(), grid, dim3(kDecThreads), 0, s, a);
+    hipLaunchKernelGGL(decode_gateup_kernel<8>, grid, dim3(kDecThreads), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipSuccess;
 }
-
-template <int GPW>
-struct GateUpSel {
-  static auto fn() { return decode_gateup_kernel<GPW>; }
-};
-template <int GPW>
-struct DownSel {
-  static auto fn() { return decode_down_kernel<GPW>; }
-};
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
   const PackGeom gu = pack_geom(a.I, a.H, 1);
   const PackGeom dn = pack_geom(a.H, a.I, 0);
-  if (gu.G > kMaxGroups || dn.G > kMaxGroups || a.T > kDecodeMaxT) return hipErrorInvalidValue;
-  const int slots = a.k * a.T + 1;
+  if (gu.G > kMaxGroups || dn.G > kMaxGroups || a.T > kDecodeMaxT || a.k != kK)
+    return hipErrorInvalidValue;
+  const int slots = kK * a.T + 1;  // unique routed experts (at most k*T), then the shared expert
   hipError_t e = hipSuccess;
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return e;
   hipLaunchKernelGGL(decode_router_kernel, dim3(a.E), dim3(256), 0, s, a);
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return e;
-  if ((e = launch_gpw<GateUpSel>(gu.G, dim3(slots * gu.n_wt), s, a)) != hipSuccess) return e;
+  if ((e = launch_gateup(gu.G, dim3(slots * gu.n_wt * 2), s, a)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return e;
-  if ((e = launch_gpw<DownSel>(dn.G, dim3(slots * dn.n_wt), s, a)) != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_down_kernel, dim3(dn.n_wt * 2), dim3(kDecThreads), 0, s, a);
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return e;
-  if ((e = launch_combine(a.partial, a.topk_w, a.y, a.T, a.H, a.k, s)) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[4], s)) != hipSuccess) return e;
   return hipGetLastError();
 }
 

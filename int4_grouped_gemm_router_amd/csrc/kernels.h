@@ -85,12 +85,12 @@ struct DecodeArgs {
   const uint8_t* dn_shared;
   int64_t dn_expert_bytes;
   uint16_t* h;                // [k*T + T][I] bf16 (slot order: pairs, then shared)
-  float* partial;             // [T][k+1][H] fp32 (slot k: shared expert)
   uint16_t* y;                // [T][H]
   int T, H, I, E, k, block_m;
 };
 
-// ev (optional): five events recorded before each of the four launches and after the last.
+// ev (optional): four events recorded before each of the three launches and after the last.
+// Requires k == 8.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev = nullptr);
 
 }  // namespace moe

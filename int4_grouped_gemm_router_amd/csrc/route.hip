@@ -109,7 +109,6 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
 
 // Grid: ceil(T/4); one wave per token.
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
-  __shared__ uint32_t scratch[4][24];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= a.T) return;
@@ -142,7 +141,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   for (int i = 0; i < 4; ++i) key[i] = i < per ? logit_key(l[i]) : 0u;
   int sel_e;
   float sel_l;
-  wave_topk(key, l, k, lane, scratch[wave], sel_e, sel_l);
+  wave_topk(key, l, k, lane, sel_e, sel_l);
   const float top = __shfl(sel_l, 0);
   // weights: exp(l_j - l_0) / sum over the k selected
   const float p = lane < k ? expf(sel_l - top) : 0.f;
