@@ -12,8 +12,8 @@
 // persistent: every block streams its units back to back and starts loading
 // the next unit while the current one finishes, so the memory pipeline does
 // not drain between units. Two kernels share the per-group arithmetic:
-//   gemm_ring_kernel    K a multiple of 512 (the main path): register ring of
-//                       plain loads, seven groups ahead, see below;
+//   gemm_ring_kernel    K a multiple of 256 (the main path): register ring of
+//                       plain loads, three groups ahead, see below;
 //   gemm_stream_kernel  any other K: an LDS ring filled by asynchronous
 //                       global -> LDS copies with explicit vmcnt waits.
 //
@@ -110,25 +110,19 @@ __device__ __forceinline__ void ring_step(const u32x4 w0, const u32x4 w1, const 
     xsv[ms] = mfma16(ax[ms][0], ones, f32x4{0.f, 0.f, 0.f, 0.f});
     xsv[ms] = mfma16(ax[ms][1], ones, xsv[ms]);
   }
-  f32x4 p[NS][4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     const u32x4 b0 = expand_codes(words[2 * ct], xk);
     const u32x4 b1 = expand_codes(words[2 * ct + 1], xk);
-#pragma unroll
-    for (int ms = 0; ms < NS; ++ms) {
-      p[ms][ct] = mfma16(ax[ms][0], b0, f32x4{0.f, 0.f, 0.f, 0.f});
-      p[ms][ct] = mfma16(ax[ms][1], b1, p[ms][ct]);
-    }
-  }
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
     const float bp = bi[ct] - 128.0f * sc[ct];
 #pragma unroll
-    for (int ms = 0; ms < NS; ++ms)
+    for (int ms = 0; ms < NS; ++ms) {
+      f32x4 p = mfma16(ax[ms][0], b0, f32x4{0.f, 0.f, 0.f, 0.f});
+      p = mfma16(ax[ms][1], b1, p);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        acc[ms][ct][i] = __builtin_fmaf(bp, xsv[ms][i], __builtin_fmaf(sc[ct], p[ms][ct][i], acc[ms][ct][i]));
+        acc[ms][ct][i] = __builtin_fmaf(bp, xsv[ms][i], __builtin_fmaf(sc[ct], p[i], acc[ms][ct][i]));
+    }
   }
 }
 
@@ -329,22 +323,24 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs a) {
 
 // ------------------------------------------------------------------ register-ring kernel
 //
-// The main path for K a multiple of 512 (G % 8 == 0). Two blocks of four waves
-// per compute unit; each wave owns 64 columns. Every load of the loop is a
-// plain register load: per wave and group the packed codes (2 KB), a 1 KB
-// share of the gathered activation rows and a 256-byte share of the
-// scale/bias words are loaded into an eight-deep register ring seven groups
-// ahead (about 110 KB per compute unit in flight). At its turn a group's
+// The main path for K a multiple of 256 (G % 4 == 0). Three blocks of four
+// waves per compute unit (three waves per SIMD, so one wave's waits are
+// covered by the others); each wave owns 64 columns. Every load of the loop
+// is a plain register load: per wave and group the packed codes (2 KB), a
+// 1 KB share of the gathered activation rows and a 256-byte share of the
+// scale/bias words are loaded into a four-deep register ring three groups
+// ahead (about 120 KB per compute unit in flight). At its turn a group's
 // activation and scale/bias shares are written to a two-stage LDS buffer, one
 // barrier, and all four waves read them. Unit boundaries fall on multiples of
-// eight groups, so every ring slot index is static and the loads for the next
+// four groups, so every ring slot index is static and the loads for the next
 // unit start while the current one finishes. Loads of one kind complete in
-// order, so the compiler's own wait counts keep seven groups in flight (no
+// order, so the compiler's own wait counts keep three groups in flight (no
 // asynchronous LDS copies are mixed in, which would force full drains).
 
 constexpr int kRWaves = 4;
 constexpr int kRThreads = kRWaves * 64;
-constexpr int kRS = 8;  // ring depth in groups
+constexpr int kRS = 4;         // ring depth in groups (K / 64 must be a multiple)
+constexpr int kRBlocksPerCU = 3;
 
 struct RingLds {
   u32x4 x[2][kXBytes / 16];      // [stage][ms 2][c 8][row 16]
@@ -356,7 +352,7 @@ struct RingLds {
 };
 
 template <int MODE>
-__global__ __launch_bounds__(kRThreads, 2) void gemm_ring_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kRThreads, kRBlocksPerCU) void gemm_ring_kernel(GemmArgs a) {
   __shared__ RingLds L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -473,7 +469,7 @@ __global__ __launch_bounds__(kRThreads, 2) void gemm_ring_kernel(GemmArgs a) {
 #pragma unroll
       for (int d = 0; d < kRS; ++d) {
         const int nx = (d + kRS - 1) % kRS;
-        load(rc[nx][0], rc[nx][1], rx[nx], rb[nx]);  // group s0 + d + 7 (or a repeat of the last)
+        load(rc[nx][0], rc[nx][1], rx[nx], rb[nx]);  // group s0 + d + kRS - 1 (or a repeat of the last)
         L.x[d & 1][xu] = rx[d];
         reinterpret_cast<uint32_t*>(&L.sb[d & 1][wave][0])[lane] = rb[d];
         // this group's shares are in LDS, and every wave is done with the
@@ -632,7 +628,7 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
   if (G < 2 || G > kMaxGroups) return hipErrorInvalidValue;
   const int cus = persistent_blocks();
   if (G % kRS == 0) {
-    const dim3 grid(2 * cus), block(kRThreads);
+    const dim3 grid(kRBlocksPerCU * cus), block(kRThreads);
     hipLaunchKernelGGL(gemm_ring_kernel<MODE>, grid, block, 0, s, a);
     return hipGetLastError();
   }
