@@ -279,6 +279,16 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     log(f"device: {torch.cuda.get_device_name(0)}")
 
+    if args.workload.startswith("decode"):
+        # decode alone (for profiling): the GEMV bandwidth line of that workload
+        r = run_decode(args.workload, args.decode_steps, 20, 32)
+        log(f"{args.workload}: {r}")
+        print(json.dumps({"metric": METRIC, "value": r["gemv_gbs"], "unit": "GB/s", "n_gpus": 1,
+                          "steps": r["steps"], "warmup": 20, "ms_per_step": r["ms_per_step"],
+                          "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                          "dtype": "bf16", "data": "synthetic",
+                          "config": {"workload": args.workload, "T": r["T"]}, "decode": r}), flush=True)
+        return
     res, (w, x) = run_prefill(args.workload, args.steps, args.warmup, args.copies)
     log(f"{args.workload}: {res}")
     gu_us = res["kernels_us"]["gemm_gateup"]
