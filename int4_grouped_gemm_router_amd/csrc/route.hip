@@ -113,14 +113,19 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const int t = blockIdx.x * 4 + wave;
   if (t >= a.T) return;
   const int E = a.E, k = a.k, per = E / 64;
-  // all partial loads first (splits <= kMaxSplits), then a fixed-order sum
-  float pv[kMaxSplits][4];
+  // all partial and bias loads first (splits <= kMaxSplits; unconditional,
+  // clamped loads, so that no branch separates them and they share one
+  // memory round trip), then a fixed-order sum
+  float pv[kMaxSplits][4], rb[4];
+  const float* rbias = a.rbias ? a.rbias : a.partial;  // read but unused without a bias
 #pragma unroll
   for (int sp = 0; sp < kMaxSplits; ++sp)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      pv[sp][i] = (sp < a.splits && i < per) ? a.partial[((int64_t)sp * a.T + t) * E + lane + 64 * i]
-                                             : 0.f;
+      pv[sp][i] = a.partial[((int64_t)min(sp, a.splits - 1) * a.T + t) * E + lane + 64 * min(i, per - 1)];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rb[i] = rbias[lane + 64 * min(i, per - 1)];
+  __builtin_amdgcn_sched_barrier(0);
   float l[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -129,8 +134,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
       const int e = lane + 64 * i;
       float v = 0.f;
 #pragma unroll
-      for (int sp = 0; sp < kMaxSplits; ++sp) v += pv[sp][i];
-      if (a.rbias) v += a.rbias[e];
+      for (int sp = 0; sp < kMaxSplits; ++sp) v += sp < a.splits ? pv[sp][i] : 0.f;
+      if (a.rbias) v += rb[i];
       if (a.logits_out) a.logits_out[(int64_t)t * E + e] = v;
       l[i] = v == v ? v : -INFINITY;  // a NaN logit ranks as -inf
     }
@@ -186,20 +191,24 @@ __global__ __launch_bounds__(256) void scan_scatter_kernel(ScatterArgs a) {
   const int n_chunks = (P + kChunkPairs - 1) / kChunkPairs;
   // this wave's pair ids, loaded before the scan so both round trips overlap
   const int p0 = chunk * kChunkPairs + wave * 256;
+  // (clamped, unconditional loads: no branch separates them)
   int pe[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int p = p0 + r * 64 + lane;
-    pe[r] = p < P ? a.topk_idx[p] : 0;
-  }
-  // totals and this chunk's base per expert
+  for (int r = 0; r < 4; ++r) pe[r] = a.topk_idx[min(p0 + r * 64 + lane, P - 1)];
+  // totals and this chunk's base per expert, eight chunk counts per round trip
   int tot = 0, before = 0;
-  if (tid < E) {
-#pragma unroll 8
-    for (int c = 0; c < n_chunks; ++c) {
-      const int v = a.chunk_hist[c * E + tid];
-      tot += v;
-      if (c < chunk) before += v;
+  const int te = min(tid, E - 1);
+  for (int c0 = 0; c0 < n_chunks; c0 += 8) {
+    int v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = a.chunk_hist[min(c0 + c, n_chunks - 1) * E + te];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int cc = c0 + c;
+      if (cc < n_chunks && tid < E) {
+        tot += v[c];
+        if (cc < chunk) before += v[c];
+      }
     }
   }
   int total;
