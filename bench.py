@@ -18,8 +18,12 @@ Prints ONE JSON line on stdout (progress goes to stderr):
                 flops per launch / its mean duration from HIP events recorded
                 on the library's stream around every launch in the timed region
   cpu_baseline  the CPU oracle timed on this host on the same workload
-  secondary     the 2048-token Zipf-skewed prefill (bf16 MFMA fraction) and
-                batch-1 decode (HBM GB/s of the GEMV kernels), same method
+  secondary     the 2048-token Zipf-skewed prefill (bf16 MFMA fraction), the
+                16384-token prompt in 4096-token chunks, and batch-1 and
+                batch-4 decode (HBM GB/s of the GEMV kernels), same method
+
+--sweep-chunks prints instead one JSON line with the 16384-token prompt
+timed at chunk sizes 1024 .. 16384 (throughput against workspace size).
 """
 from __future__ import annotations
 
@@ -80,7 +84,7 @@ def _graph_of(calls):
     return g
 
 
-def run_prefill(name, steps, warmup, copies):
+def run_prefill(name, steps, warmup, copies, chunk=None, block_m=32):
     """Time `steps` layer calls. The step time (value) comes from replaying a
     HIP graph of `copies` consecutive layer calls (one per weight copy); the
     per-kernel durations come from HIP events recorded on the library's
@@ -88,9 +92,10 @@ def run_prefill(name, steps, warmup, copies):
     import torch
     from int4_grouped_gemm_router_amd import binding as B
     wl, w, x, xd, dws = prefill_setup(name, copies)
-    d = dws[0].dims
+    d0 = dws[0].dims
+    d = B.dims(d0.H, d0.I, d0.E, d0.top_k, block_m)
     T, H, I = wl.T, wl.H, wl.I
-    chunk = wl.chunk
+    chunk = wl.chunk if chunk is None else chunk
     Tc = chunk if chunk else T
     chunks = -(-T // Tc)
     y = torch.empty((T, H), dtype=torch.int16, device="cuda")
@@ -265,6 +270,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--block-m", type=int, default=32, choices=(16, 32),
+                    help="routing block size = GEMM work-item rows (ablation; 32 by default)")
+    ap.add_argument("--sweep-chunks", action="store_true",
+                    help="time the 16384-token prompt at several chunk sizes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -279,6 +288,20 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     log(f"device: {torch.cuda.get_device_name(0)}")
 
+    if args.sweep_chunks:
+        from int4_grouped_gemm_router_amd import binding as B
+        sweep = []
+        for c in (1024, 2048, 4096, 8192, 16384):
+            r, (w, _) = run_prefill("long_t16384", 10, 2, args.copies, chunk=c)
+            ws_bytes = B.moe_workspace_bytes(B.MoeDims(w.H, w.I, w.E, 8, 32), c, B.MODE_PREFILL)
+            row = {"chunk": c, "ms_per_step": r["ms_per_step"], "tokens_per_s": r["tokens_per_s"],
+                   "expert_tflops": r["expert_tflops"], "workspace_bytes": ws_bytes,
+                   "kernels_us_per_chunk": r["kernels_us"]}
+            log(f"chunk {c}: {row}")
+            sweep.append(row)
+        print(json.dumps({"metric": METRIC, "workload": "long_t16384", "unit": "tokens/s",
+                          "sweep": sweep}), flush=True)
+        return
     if args.workload.startswith("decode"):
         # decode alone (for profiling): the GEMV bandwidth line of that workload
         r = run_decode(args.workload, args.decode_steps, 20, 32)
@@ -289,7 +312,8 @@ def main():
                           "dtype": "bf16", "data": "synthetic",
                           "config": {"workload": args.workload, "T": r["T"]}, "decode": r}), flush=True)
         return
-    res, (w, x) = run_prefill(args.workload, args.steps, args.warmup, args.copies)
+    res, (w, x) = run_prefill(args.workload, args.steps, args.warmup, args.copies,
+                              block_m=args.block_m)
     log(f"{args.workload}: {res}")
     gu_us = res["kernels_us"]["gemm_gateup"]
     dominant = max(res["kernels_us"], key=res["kernels_us"].get)
@@ -316,6 +340,7 @@ def main():
                    "top_k": 8, "shared_experts": 1,
                    "weights": "int4 affine, groups of 64, bf16 scale+bias",
                    "weight_copies": args.copies, "launch": "hip graph per layer call",
+                   "block_m": args.block_m,
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "kernels_us": res["kernels_us"],
@@ -330,9 +355,15 @@ def main():
         r2, _ = run_prefill("skew_t2048", max(10, args.steps // 2), args.warmup, args.copies)
         log(f"skew_t2048: {r2}")
         sec.append(r2)
+        r4, _ = run_prefill("long_t16384", 10, 2, args.copies)
+        log(f"long_t16384: {r4}")
+        sec.append(r4)
         r3 = run_decode("decode_t1", args.decode_steps, 20, 32)
         log(f"decode_t1: {r3}")
         sec.append(r3)
+        r5 = run_decode("decode_t4", args.decode_steps, 20, 32)
+        log(f"decode_t4: {r5}")
+        sec.append(r5)
         out["secondary"] = sec
     print(json.dumps(out), flush=True)
 

@@ -27,8 +27,12 @@
  *    surface at the caller's next synchronisation.
  *  - Return value: MOE_OK (0) or a negative MOE_E* code. Arguments are checked
  *    before anything is enqueued, so on error nothing has been launched.
- *  - Supported dims: E <= 256 and E % 64 == 0, top_k == 8, block_m == 32,
- *    H % 256 == 0 (H <= 4096), I % 128 == 0 (I <= 4096).
+ *  - Supported dims: E <= 256 and E % 64 == 0, top_k == 8, block_m 32 or 16
+ *    (the routing block size, which is also the row count of the grouped
+ *    GEMMs' work items; diariobitcoin.com, "Perplexity libera Lily...",
+ *    section "Las optimizaciones en el prefill": 32-row blocks replaced
+ *    16-row ones), H % 256 == 0 (H <= 4096), I % 128 == 0
+ *    (I <= 4096).
  */
 #ifndef MOE_INT4_H
 #define MOE_INT4_H

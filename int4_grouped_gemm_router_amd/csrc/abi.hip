@@ -10,7 +10,7 @@ using namespace moe;
 namespace {
 
 bool dims_ok(const moe_dims* d) {
-  return d && d->E > 0 && d->E <= 256 && d->E % 64 == 0 && d->top_k == 8 && d->block_m == 32 &&
+  return d && d->E > 0 && d->E <= 256 && d->E % 64 == 0 && d->top_k == 8 && (d->block_m == 32 || d->block_m == 16) &&
          d->H > 0 && d->H % 256 == 0 && d->H <= 4096 && d->I > 0 && d->I % 128 == 0 &&
          d->I <= 4096;
 }
@@ -20,7 +20,7 @@ int64_t max_blocks(const moe_dims* d, int T) {
 }
 
 int max_items(const moe_dims* d, int T) {
-  return (int)(((int64_t)d->top_k * T + kItemRows - 1) / kItemRows + d->E);
+  return (int)(((int64_t)d->top_k * T + d->block_m - 1) / d->block_m + d->E);
 }
 
 int n_chunks(const moe_dims* d, int T) {
@@ -292,13 +292,15 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
     sa.E = E;
     sa.k = k;
     sa.block_m = dims->block_m;
+    sa.item_rows = dims->block_m;  // one GEMM work item per routing block
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;
     if (launch_scan_scatter(sa, s) != hipSuccess) return MOE_EHIP;
 
     GemmArgs g{};
     g.items = W.items;
     g.num_items = W.num_items;
-    g.shared_slots = (Tn + kItemRows - 1) / kItemRows;
+    g.item_rows = dims->block_m;
+    g.shared_slots = (Tn + g.item_rows - 1) / g.item_rows;
     g.T = Tn;
     g.k = k;
     g.perm = sa.perm;

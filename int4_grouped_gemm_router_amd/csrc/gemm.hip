@@ -73,7 +73,7 @@ __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
 struct UnitInfo {
   int expert;  // -1: shared expert
   int row0;    // first row (sorted pair position, or k*T + first token for the shared expert)
-  int rows;    // 1..kItemRows
+  int rows;    // 1..item_rows
   int nt;      // column tile
 };
 
@@ -172,10 +172,10 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs a) {
         u.row0 = a.items[3 * slot + 1];
         u.rows = a.items[3 * slot + 2];
       } else {
-        const int t0 = (slot - ni) * kItemRows;
+        const int t0 = (slot - ni) * a.item_rows;
         u.expert = -1;
         u.row0 = a.k * a.T + t0;
-        u.rows = min(kItemRows, a.T - t0);
+        u.rows = min(a.item_rows, a.T - t0);
       }
       L.unit[tid] = u;
     }
@@ -388,10 +388,10 @@ __global__ __launch_bounds__(kRThreads, kRBlocksPerCU) void gemm_ring_kernel(Gem
         u.row0 = a.items[3 * slot + 1];
         u.rows = a.items[3 * slot + 2];
       } else {
-        const int t0 = (slot - ni) * kItemRows;
+        const int t0 = (slot - ni) * a.item_rows;
         u.expert = -1;
         u.row0 = a.k * a.T + t0;
-        u.rows = min(kItemRows, a.T - t0);
+        u.rows = min(a.item_rows, a.T - t0);
       }
       L.unit[tid] = u;
     }

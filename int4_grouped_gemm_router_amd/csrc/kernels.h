@@ -11,7 +11,7 @@
 namespace moe {
 
 constexpr int kChunkPairs = 1024;  // (token, slot) pairs per scatter block
-constexpr int kItemRows = 32;      // rows of one expert per GEMM work item (one routing block)
+constexpr int kItemRows = 32;      // most rows of one expert per GEMM work item (one routing block)
 constexpr int kMaxGroups = 64;     // K / 64 upper bound of the expert GEMMs
 constexpr int kDecodeMaxT = 4;
 constexpr int kMaxSplits = 8;      // router K splits summed by the top-k kernel
@@ -33,6 +33,7 @@ struct ScatterArgs {
   int32_t *hist, *offsets, *perm, *inv_perm, *block_map, *num_blocks;
   int32_t *items, *num_items;  // GEMM work list or null
   int T, E, k, block_m;
+  int item_rows;               // rows per GEMM work item (<= kItemRows)
 };
 
 // Which GEMM: gate/up with SwiGLU, or down (routed and shared items) writing
@@ -42,7 +43,8 @@ enum GemmMode { kGateUp = 0, kDown = 1 };
 struct GemmArgs {
   const int32_t* items;      // routed work list [max][3] (expert, first row, rows)
   const int32_t* num_items;  // device scalar
-  int shared_slots;          // shared-expert items (kItemRows tokens each)
+  int shared_slots;          // shared-expert items (item_rows tokens each)
+  int item_rows;             // rows per work item, <= kItemRows (the routing block size)
   const uint8_t* blob;       // routed experts (past the header)
   const uint8_t* shared_blob;
   int64_t expert_bytes;

@@ -231,16 +231,17 @@ __global__ __launch_bounds__(256) void scan_scatter_kernel(ScatterArgs a) {
       bm[2] = min(a.block_m, tot - i * a.block_m);
     }
     if (tid == 0) *a.num_blocks = nb_total;
-    // GEMM work items: up to kItemRows rows of one expert
+    // GEMM work items: up to item_rows rows of one expert
     if (a.items) {
       int ni_total;
-      const int ni = tid < E ? (tot + kItemRows - 1) / kItemRows : 0;
+      const int ir = a.item_rows;
+      const int ni = tid < E ? (tot + ir - 1) / ir : 0;
       const int ioff = block_exclusive_scan(ni, scratch, ni_total);
       for (int i = 0; i < ni; ++i) {
         int* it = a.items + 3 * (int64_t)(ioff + i);
         it[0] = tid;
-        it[1] = off + i * kItemRows;
-        it[2] = min(kItemRows, tot - i * kItemRows);
+        it[1] = off + i * ir;
+        it[2] = min(ir, tot - i * ir);
       }
       if (tid == 0) *a.num_items = ni_total;
     }

@@ -86,6 +86,34 @@ def test_prefill_t512_all_tokens(torch_cuda):
     print(f"T=512: {s}")
 
 
+def test_prefill_t512_block16(torch_cuda):
+    # 16-row routing blocks, which are also the GEMMs' work items: the block
+    # map follows the oracle's for BM = 16, and y equals the 32-row run bit
+    # for bit (every output row is computed alone, in the same order)
+    torch = torch_cuda
+    wl, w, dw = _layer("prefill_t512")
+    _, _, x = synth.generate("prefill_t512", with_x=True)
+    T = x.shape[0]
+    y32, logits32, _ = _prefill(torch, dw, x)
+    d16 = B.dims(w.H, w.I, block_m=16)
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty((T, w.H), dtype=torch.int16, device="cuda")
+    logits = torch.empty((T, w.E), dtype=torch.float32, device="cuda")
+    ro = B.RouteBuffers(d16, T)
+    B.moe_prefill_layer(d16, dw, xd, y, T, 0, logits, ro, B.workspace(d16, T, B.MODE_PREFILL))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().view(np.uint16)
+    meta = ro.to_numpy()
+    idx, wsel = _route_of(meta, T)
+    check_route_meta(meta, idx, 256, 8, 16)
+    ref = oracle.route_meta(idx, 256, 16)
+    assert np.array_equal(meta["block_map"], ref["block_map"])
+    assert np.array_equal(logits.cpu().numpy(), logits32)
+    assert np.array_equal(y, y32), "16-row and 32-row work items differ"
+    s = check_layer(x, w, y, logits.cpu().numpy(), idx, wsel, tokens=np.arange(0, T, 7))
+    print(f"T=512 block_m 16: {s}")
+
+
 def test_prefill_skew_t2048_sampled(torch_cuda):
     wl, w, dw = _layer("skew_t2048")
     _, _, x = synth.generate("skew_t2048", with_x=True)
