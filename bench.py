@@ -272,6 +272,10 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--block-m", type=int, default=32, choices=(16, 32),
                     help="routing block size = GEMM work-item rows (ablation; 32 by default)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="ablation: time moe_prefill_layer_unfused against the fused call")
+    ap.add_argument("--host-routing", action="store_true",
+                    help="ablation: time moe_prefill_layer_host_routed against the GPU-routed call")
     ap.add_argument("--sweep-chunks", action="store_true",
                     help="time the 16384-token prompt at several chunk sizes")
     args = ap.parse_args()
@@ -288,6 +292,61 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     log(f"device: {torch.cuda.get_device_name(0)}")
 
+    if args.unfused:
+        from int4_grouped_gemm_router_amd import binding as B
+        rows = []
+        for name in ("prefill_t512", "skew_t2048"):
+            r, _ = run_prefill(name, args.steps, args.warmup, args.copies)
+            wl, w, x, xd, dws = prefill_setup(name, args.copies)
+            d = dws[0].dims
+            T = wl.T
+            y = torch.empty((T, w.H), dtype=torch.int16, device="cuda")
+            ws = B.workspace(d, T, B.MODE_PREFILL)
+            wbuf = B.unfused_weights(d)
+            for i in range(args.warmup):
+                B.moe_prefill_layer_unfused(d, dws[i % args.copies], xd, y, T, wbuf, ws=ws)
+            graphs = [_graph_of(lambda i=i: B.moe_prefill_layer_unfused(d, dws[i], xd, y, T, wbuf, ws=ws))
+                      for i in range(args.copies)]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                graphs[i % args.copies].replay()
+            torch.cuda.synchronize()
+            ms_unf = (time.perf_counter() - t0) * 1e3 / args.steps
+            row = {"workload": name, "T": T, "ms_fused": r["ms_per_step"], "ms_unfused": ms_unf,
+                   "speedup_fused": ms_unf / r["ms_per_step"], "bf16_weight_buffer_bytes": wbuf.numel()}
+            log(f"unfused {name}: {row}")
+            rows.append(row)
+        print(json.dumps({"metric": METRIC, "ablation": "fused vs unfused dequant", "rows": rows}),
+              flush=True)
+        return
+    if args.host_routing:
+        from int4_grouped_gemm_router_amd import binding as B
+        rows = []
+        for name in ("prefill_t512", "skew_t2048"):
+            r, _ = run_prefill(name, args.steps, args.warmup, args.copies)
+            wl, w, x, xd, dws = prefill_setup(name, args.copies)
+            d = dws[0].dims
+            T = wl.T
+            y = torch.empty((T, w.H), dtype=torch.int16, device="cuda")
+            ws = B.workspace(d, T, B.MODE_PREFILL)
+            for i in range(args.warmup):
+                B.moe_prefill_layer_host_routed(d, dws[i % args.copies], xd, y, T, 0, ws)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                B.moe_prefill_layer_host_routed(d, dws[i % args.copies], xd, y, T, 0, ws)
+            torch.cuda.synchronize()
+            ms_host = (time.perf_counter() - t0) * 1e3 / args.steps
+            row = {"workload": name, "T": T, "ms_gpu_routed_graph": r["ms_per_step"],
+                   "ms_gpu_routed_eager": r["ms_per_step_eager"], "ms_host_routed": ms_host,
+                   "speedup_gpu_routed_eager": ms_host / r["ms_per_step_eager"],
+                   "speedup_gpu_routed_graph": ms_host / r["ms_per_step"]}
+            log(f"host routing {name}: {row}")
+            rows.append(row)
+        print(json.dumps({"metric": METRIC, "ablation": "host-synchronised routing", "rows": rows}),
+              flush=True)
+        return
     if args.sweep_chunks:
         from int4_grouped_gemm_router_amd import binding as B
         sweep = []

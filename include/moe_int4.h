@@ -166,6 +166,35 @@ int moe_decode_layer(const moe_dims* dims, const moe_layer_weights* w, const uin
                      uint16_t* y, int32_t T, float* logits_out, const moe_route_out* route_out,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* The prefill layer with host-synchronised routing, for measuring what
+ * GPU-resident routing saves (diariobitcoin.com, "Perplexity libera Lily...",
+ * section "Las optimizaciones en el prefill": keeping histogram, scan,
+ * scatter and block map on the GPU, with no CPU round trip, sped prefill
+ * up). Same arguments and results as moe_prefill_layer (no logits or
+ * metadata outputs), but per chunk the calling thread waits for the routing
+ * kernels, reads the work-item count back (4 bytes, device -> host) and
+ * launches the grouped GEMMs with grids of exactly one block per work unit
+ * instead of the persistent grids. It synchronises the host once per chunk,
+ * so it cannot be captured in a graph. */
+int moe_prefill_layer_host_routed(const moe_dims* dims, const moe_layer_weights* w,
+                                  const uint16_t* x, uint16_t* y, int32_t T, int32_t chunk_T,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/* The prefill layer without fused dequantisation, for measuring what the
+ * fusion saves (diariobitcoin.com, "Perplexity libera Lily...", section "Las
+ * optimizaciones en el prefill": reconstructing the weights inside the
+ * grouped GEMM, never writing them back, sped prefill up). Per chunk, after
+ * the routing, every expert with rows and the shared expert are expanded to
+ * bf16 w = q*s + b (one rounding) into wbuf (device, caller-owned,
+ * moe_unfused_weight_bytes bytes), then the grouped GEMMs read those bf16
+ * weights. Same results as moe_prefill_layer up to the bf16 rounding of the
+ * weights (no logits or metadata outputs). MOE_EBUFFER if wbuf is too
+ * small. */
+int moe_unfused_weight_bytes(const moe_dims* dims, size_t* bytes);
+int moe_prefill_layer_unfused(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x,
+                              uint16_t* y, int32_t T, int32_t chunk_T, void* wbuf, size_t wbuf_bytes,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* Timing variants for benchmarks: identical to moe_prefill_layer /
  * moe_decode_layer, and in addition record the caller's events (hipEvent_t
  * handles created by the caller) on `stream`: events[i] just before the i-th

@@ -83,13 +83,20 @@ def lib():
         L.moe_decode_layer.argtypes = [P(MoeDims), P(MoeLayerWeights), _vp, _vp, _i32, _vp,
                                        P(MoeRouteOut), _vp, _sz, _vp]
         L.moe_prefill_layer_profiled.argtypes = L.moe_prefill_layer.argtypes + [_vp, _i32]
+        L.moe_prefill_layer_host_routed.argtypes = [P(MoeDims), P(MoeLayerWeights), _vp, _vp, _i32,
+                                                    _i32, _vp, _sz, _vp]
+        L.moe_unfused_weight_bytes.argtypes = [P(MoeDims), P(_sz)]
+        L.moe_prefill_layer_unfused.argtypes = [P(MoeDims), P(MoeLayerWeights), _vp, _vp, _i32, _i32,
+                                                _vp, _sz, _vp, _sz, _vp]
         L.moe_decode_layer_profiled.argtypes = L.moe_decode_layer.argtypes + [_vp, _i32]
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
         L.moe_test_dequant.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp]
         for name in ("pack_int4_g64", "pack_router_bf16x3", "moe_workspace_bytes", "moe_route",
                      "moe_prefill_layer", "moe_decode_layer", "moe_test_dequant",
-                     "moe_prefill_layer_profiled", "moe_decode_layer_profiled"):
+                     "moe_prefill_layer_profiled", "moe_decode_layer_profiled",
+                     "moe_prefill_layer_host_routed", "moe_unfused_weight_bytes",
+                     "moe_prefill_layer_unfused"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -274,6 +281,30 @@ def moe_prefill_layer(d: MoeDims, w: DeviceWeights, x, y, T: int, chunk_T: int =
                                    chunk_T, _ptr(logits_out), ro, _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream(stream)),
            "moe_prefill_layer")
+
+
+def moe_prefill_layer_host_routed(d: MoeDims, w: DeviceWeights, x, y, T: int, chunk_T: int = 0,
+                                  ws=None, stream=None):
+    _check(lib().moe_prefill_layer_host_routed(ctypes.byref(d), ctypes.byref(w.struct), _ptr(x),
+                                               _ptr(y), T, chunk_T, _ptr(ws),
+                                               0 if ws is None else ws.numel(), _stream(stream)),
+           "moe_prefill_layer_host_routed")
+
+
+def unfused_weights(d: MoeDims, device="cuda"):
+    """Device buffer for moe_prefill_layer_unfused's bf16 weights."""
+    import torch
+    n = _sz(0)
+    _check(lib().moe_unfused_weight_bytes(ctypes.byref(d), ctypes.byref(n)), "moe_unfused_weight_bytes")
+    return torch.empty(n.value, dtype=torch.uint8, device=device)
+
+
+def moe_prefill_layer_unfused(d: MoeDims, w: DeviceWeights, x, y, T: int, wbuf, chunk_T: int = 0,
+                              ws=None, stream=None):
+    _check(lib().moe_prefill_layer_unfused(ctypes.byref(d), ctypes.byref(w.struct), _ptr(x), _ptr(y), T,
+                                           chunk_T, _ptr(wbuf), wbuf.numel(), _ptr(ws),
+                                           0 if ws is None else ws.numel(), _stream(stream)),
+           "moe_prefill_layer_unfused")
 
 
 def moe_decode_layer(d: MoeDims, w: DeviceWeights, x, y, T: int, logits_out=None,

@@ -131,7 +131,8 @@ constexpr int kDecodeLaunches = 3;
 
 int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x, uint16_t* y,
                  int32_t T, int32_t chunk_T, float* logits_out, const moe_route_out* route_out,
-                 void* ws, size_t ws_bytes, void* stream, Recorder rec);
+                 void* ws, size_t ws_bytes, void* stream, Recorder rec, bool host_routed = false,
+                 uint8_t* unfused_w = nullptr);
 int decode_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x, uint16_t* y,
                 int32_t T, float* logits_out, const moe_route_out* route_out, void* ws,
                 size_t ws_bytes, void* stream, hipEvent_t* ev);
@@ -208,6 +209,34 @@ int moe_prefill_layer(const moe_dims* dims, const moe_layer_weights* w, const ui
                       Recorder{});
 }
 
+int moe_prefill_layer_host_routed(const moe_dims* dims, const moe_layer_weights* w,
+                                  const uint16_t* x, uint16_t* y, int32_t T, int32_t chunk_T,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  return prefill_impl(dims, w, x, y, T, chunk_T, nullptr, nullptr, ws, ws_bytes, stream,
+                      Recorder{}, true);
+}
+
+int moe_unfused_weight_bytes(const moe_dims* dims, size_t* bytes) {
+  if (!bytes) return MOE_EINVAL;
+  if (!dims_ok(dims)) return MOE_EUNSUPPORTED;
+  const PackGeom gu = pack_geom(dims->I, dims->H, 1), dn = pack_geom(dims->H, dims->I, 0);
+  *bytes = (size_t)(dims->E + 1) *
+           ((size_t)gu.n_wt * gu.G + (size_t)dn.n_wt * dn.G) * kBf16GroupBytes;
+  return MOE_OK;
+}
+
+int moe_prefill_layer_unfused(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x,
+                              uint16_t* y, int32_t T, int32_t chunk_T, void* wbuf, size_t wbuf_bytes,
+                              void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  const int rc = moe_unfused_weight_bytes(dims, &need);
+  if (rc != MOE_OK) return rc;
+  if (!wbuf) return MOE_EINVAL;
+  if (wbuf_bytes < need) return MOE_EBUFFER;
+  return prefill_impl(dims, w, x, y, T, chunk_T, nullptr, nullptr, ws, ws_bytes, stream,
+                      Recorder{}, false, static_cast<uint8_t*>(wbuf));
+}
+
 int moe_prefill_layer_profiled(const moe_dims* dims, const moe_layer_weights* w,
                                const uint16_t* x, uint16_t* y, int32_t T, int32_t chunk_T,
                                float* logits_out, const moe_route_out* route_out, void* ws,
@@ -231,7 +260,8 @@ namespace {
 
 int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x, uint16_t* y,
                  int32_t T, int32_t chunk_T, float* logits_out, const moe_route_out* route_out,
-                 void* ws, size_t ws_bytes, void* stream, Recorder rec) {
+                 void* ws, size_t ws_bytes, void* stream, Recorder rec, bool host_routed,
+                 uint8_t* unfused_w) {
   if (!dims || T < 0) return MOE_EINVAL;
   if (!dims_ok(dims)) return MOE_EUNSUPPORTED;
   if (T == 0) return MOE_OK;
@@ -296,6 +326,19 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;
     if (launch_scan_scatter(sa, s) != hipSuccess) return MOE_EHIP;
 
+    // host-routed variant: the host waits for the routing, reads the work
+    // item count and launches exact grids (one block per 256-column unit)
+    int gu_blocks = 0, dn_blocks = 0;
+    if (host_routed) {
+      int32_t ni = 0;
+      if (hipMemcpyAsync(&ni, W.num_items, sizeof ni, hipMemcpyDeviceToHost, s) != hipSuccess ||
+          hipStreamSynchronize(s) != hipSuccess)
+        return MOE_EHIP;
+      const int slots = ni + (Tn + dims->block_m - 1) / dims->block_m;
+      gu_blocks = std::max(1, slots * ((gu.n_wt + 3) / 4));
+      dn_blocks = std::max(1, slots * ((dn.n_wt + 3) / 4));
+    }
+
     GemmArgs g{};
     g.items = W.items;
     g.num_items = W.num_items;
@@ -305,22 +348,48 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
     g.k = k;
     g.perm = sa.perm;
 
+    // unfused comparison path: the touched experts' weights expanded to bf16
+    // in memory first, then the same GEMMs on the bf16 weights
+    const int64_t gu_bf = (int64_t)gu.n_wt * gu.G * kBf16GroupBytes;
+    const int64_t dn_bf = (int64_t)dn.n_wt * dn.G * kBf16GroupBytes;
+    uint8_t* gu_w = unfused_w;
+    uint8_t* gu_sh = unfused_w ? gu_w + E * gu_bf : nullptr;
+    uint8_t* dn_w = unfused_w ? gu_sh + gu_bf : nullptr;
+    uint8_t* dn_sh = unfused_w ? dn_w + E * dn_bf : nullptr;
+    g.bf16_weights = unfused_w ? 1 : 0;
+
     // gate/up + SwiGLU (routed and shared items in one launch)
     g.blob = static_cast<const uint8_t*>(w->experts_gate_up) + kHeaderBytes;
     g.shared_blob = static_cast<const uint8_t*>(w->shared_gate_up) + kHeaderBytes;
     g.expert_bytes = gu.expert_bytes;
+    if (unfused_w) {
+      if (launch_expand_bf16(g.blob, gu.expert_bytes, g.shared_blob, E, sa.hist, I, H, 1, gu_w, gu_sh,
+                             s) != hipSuccess)
+        return MOE_EHIP;
+      g.blob = gu_w;
+      g.shared_blob = gu_sh;
+      g.expert_bytes = gu_bf;
+    }
     g.N = I;
     g.K = H;
     g.paired = 1;
     g.act = xc;
     g.h_out = W.h;
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;
-    if (launch_gemm(kGateUp, g, s) != hipSuccess) return MOE_EHIP;
+    if (launch_gemm(kGateUp, g, s, gu_blocks) != hipSuccess) return MOE_EHIP;
 
     // down: routed items (one output row per pair) and shared items in one launch
     g.blob = static_cast<const uint8_t*>(w->experts_down) + kHeaderBytes;
     g.shared_blob = static_cast<const uint8_t*>(w->shared_down) + kHeaderBytes;
     g.expert_bytes = dn.expert_bytes;
+    if (unfused_w) {
+      if (launch_expand_bf16(g.blob, dn.expert_bytes, g.shared_blob, E, sa.hist, H, I, 0, dn_w, dn_sh,
+                             s) != hipSuccess)
+        return MOE_EHIP;
+      g.blob = dn_w;
+      g.shared_blob = dn_sh;
+      g.expert_bytes = dn_bf;
+    }
     g.N = H;
     g.K = I;
     g.paired = 0;
@@ -328,7 +397,7 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
     g.h_out = nullptr;
     g.partial = W.partial;
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;
-    if (launch_gemm(kDown, g, s) != hipSuccess) return MOE_EHIP;
+    if (launch_gemm(kDown, g, s, dn_blocks) != hipSuccess) return MOE_EHIP;
 
     // y = bf16(shared + sum of the k weighted expert outputs)
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;

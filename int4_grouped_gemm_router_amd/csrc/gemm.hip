@@ -126,6 +126,23 @@ __device__ __forceinline__ void ring_step(const u32x4 w0, const u32x4 w1, const 
   }
 }
 
+// One group with bf16 weights already expanded in memory: w[2 ct + ks] is the
+// B operand of column tile ct and k half ks; plain MFMA accumulation.
+template <int NS>
+__device__ __forceinline__ void ring_step_bf16(const u32x4 (&w)[8], const u32x4* xst, int kb, int c16,
+                                               f32x4 (&acc)[2][4]) {
+#pragma unroll
+  for (int ms = 0; ms < NS; ++ms) {
+    const u32x4 a0 = xst[(ms * 8 + kb) * 16 + c16];
+    const u32x4 a1 = xst[(ms * 8 + 4 + kb) * 16 + c16];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      acc[ms][ct] = mfma16(a0, w[2 * ct], acc[ms][ct]);
+      acc[ms][ct] = mfma16(a1, w[2 * ct + 1], acc[ms][ct]);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ LDS-stream kernel
 //
 // The general path (any K that is a multiple of 128). One block of eight
@@ -351,8 +368,14 @@ struct RingLds {
   u32x4 tr[kRWaves][64];
 };
 
-template <int MODE>
+// BF16W: the weights come as bf16 values already expanded in memory (the
+// unfused comparison path, see bf16 expansion below) instead of int4 codes:
+// per wave and group 8 x 16 bytes per lane, a two-deep ring, no scale, bias
+// or row sums.
+template <int MODE, bool BF16W>
 __global__ __launch_bounds__(kRThreads, kRBlocksPerCU) void gemm_ring_kernel(GemmArgs a) {
+  constexpr int RS = BF16W ? 2 : kRS;  // ring depth in groups
+  constexpr int NW = BF16W ? 8 : 2;    // weight vectors per lane and group
   __shared__ RingLds L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -418,7 +441,7 @@ __global__ __launch_bounds__(kRThreads, kRBlocksPerCU) void gemm_ring_kernel(Gem
 
     // ---- load side: unit iu, group ig (stays on the last group once every
     // group is issued, so each step issues the same four loads)
-    const int total = nb * G;  // a multiple of kRS
+    const int total = nb * G;  // a multiple of RS
     int iu = 0, ig = 0, issued = 0;
     const uint16_t* xsrc = nullptr;
     const uint8_t* nsrc = nullptr;
@@ -428,17 +451,25 @@ __global__ __launch_bounds__(kRThreads, kRBlocksPerCU) void gemm_ring_kernel(Gem
       const int nt = __builtin_amdgcn_readfirstlane(L.unit[j].nt);
       const int wt = min(nt * kRWaves + wave, n_wt - 1);
       const uint8_t* eb = expert >= 0 ? a.blob + (int64_t)expert * a.expert_bytes : a.shared_blob;
-      nsrc = eb + geom.nib_off + (int64_t)wt * G * kNibBytes + lane * 16;
+      nsrc = BF16W ? eb + (int64_t)wt * G * kBf16GroupBytes + lane * 16
+                   : eb + geom.nib_off + (int64_t)wt * G * kNibBytes + lane * 16;
       bsrc = eb + geom.sb_off + (int64_t)wt * G * kSbBytes + lane * 4;
       xsrc = a.act + (int64_t)L.rowidx[j][xm] * K + 8 * xc;
     };
-    u32x4 rc[kRS][2], rx[kRS];
-    uint32_t rb[kRS];
-    auto load = [&](u32x4& c0, u32x4& c1, u32x4& xv, uint32_t& bv) {
-      c0 = *reinterpret_cast<const u32x4*>(nsrc + (int64_t)ig * kNibBytes);
-      c1 = *reinterpret_cast<const u32x4*>(nsrc + (int64_t)ig * kNibBytes + 1024);
+    u32x4 rc[RS][NW], rx[RS];
+    uint32_t rb[RS];
+    auto load = [&](u32x4 (&cw)[NW], u32x4& xv, uint32_t& bv) {
+      if constexpr (BF16W) {
+#pragma unroll
+        for (int h = 0; h < NW; ++h)
+          cw[h] = *reinterpret_cast<const u32x4*>(nsrc + (int64_t)ig * kBf16GroupBytes + 1024 * h);
+        bv = 0;
+      } else {
+        cw[0] = *reinterpret_cast<const u32x4*>(nsrc + (int64_t)ig * kNibBytes);
+        cw[1] = *reinterpret_cast<const u32x4*>(nsrc + (int64_t)ig * kNibBytes + 1024);
+        bv = *reinterpret_cast<const uint32_t*>(bsrc + (int64_t)ig * kSbBytes);
+      }
       xv = *reinterpret_cast<const u32x4*>(xsrc + ig * kGroup);
-      bv = *reinterpret_cast<const uint32_t*>(bsrc + (int64_t)ig * kSbBytes);
       if (++issued < total) {
         if (++ig == G) {
           ig = 0;
@@ -448,12 +479,12 @@ __global__ __launch_bounds__(kRThreads, kRBlocksPerCU) void gemm_ring_kernel(Gem
     };
     set_load_unit(0);
 #pragma unroll
-    for (int d = 0; d < kRS - 1; ++d) load(rc[d][0], rc[d][1], rx[d], rb[d]);
+    for (int d = 0; d < RS - 1; ++d) load(rc[d], rx[d], rb[d]);
 
     f32x4 acc[2][4];
     int rows = 0, nsub = 0, nt = 0, row0 = 0;
     bool active = false;
-    for (int s0 = 0; s0 < total; s0 += kRS) {
+    for (int s0 = 0; s0 < total; s0 += RS) {
       const int cu = s0 / G, cg0 = s0 % G;
       if (cg0 == 0) {
         rows = __builtin_amdgcn_readfirstlane(L.unit[cu].rows);
@@ -467,23 +498,30 @@ __global__ __launch_bounds__(kRThreads, kRBlocksPerCU) void gemm_ring_kernel(Gem
           for (int ct = 0; ct < 4; ++ct) acc[ms][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int d = 0; d < kRS; ++d) {
-        const int nx = (d + kRS - 1) % kRS;
-        load(rc[nx][0], rc[nx][1], rx[nx], rb[nx]);  // group s0 + d + kRS - 1 (or a repeat of the last)
+      for (int d = 0; d < RS; ++d) {
+        const int nx = (d + RS - 1) % RS;
+        load(rc[nx], rx[nx], rb[nx]);  // group s0 + d + RS - 1 (or a repeat of the last)
         L.x[d & 1][xu] = rx[d];
-        reinterpret_cast<uint32_t*>(&L.sb[d & 1][wave][0])[lane] = rb[d];
+        if constexpr (!BF16W) reinterpret_cast<uint32_t*>(&L.sb[d & 1][wave][0])[lane] = rb[d];
         // this group's shares are in LDS, and every wave is done with the
         // stage these writes replaced (read two groups ago)
         lds_barrier();
         if (active) {
-          const u32x4 sbv = L.sb[d & 1][wave][c16];
-          if (nsub == 2)
-            ring_step<2>(rc[d][0], rc[d][1], sbv, &L.x[d & 1][0], kb, c16, xk, acc);
-          else
-            ring_step<1>(rc[d][0], rc[d][1], sbv, &L.x[d & 1][0], kb, c16, xk, acc);
+          if constexpr (BF16W) {
+            if (nsub == 2)
+              ring_step_bf16<2>(rc[d], &L.x[d & 1][0], kb, c16, acc);
+            else
+              ring_step_bf16<1>(rc[d], &L.x[d & 1][0], kb, c16, acc);
+          } else {
+            const u32x4 sbv = L.sb[d & 1][wave][c16];
+            if (nsub == 2)
+              ring_step<2>(rc[d][0], rc[d][1], sbv, &L.x[d & 1][0], kb, c16, xk, acc);
+            else
+              ring_step<1>(rc[d][0], rc[d][1], sbv, &L.x[d & 1][0], kb, c16, xk, acc);
+          }
         }
       }
-      if (cg0 + kRS < G) continue;
+      if (cg0 + RS < G) continue;
 
       // ---- epilogue of unit cu
       const int wt = nt * kRWaves + wave;
@@ -569,6 +607,46 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<u32x4*>(y + t * N + n) = o;
 }
 
+// Unfused comparison path: expand packed experts to bf16 in memory. Grid:
+// (count + 1 experts, n_wt * G / 4); block: 4 waves, one (wave tile, group)
+// each; the last expert index is the shared expert.
+__global__ __launch_bounds__(256) void expand_bf16_kernel(const uint8_t* blob, int64_t expert_bytes,
+                                                          const uint8_t* shared_blob, int count,
+                                                          const int32_t* hist, int N, int K,
+                                                          int paired, uint8_t* out,
+                                                          uint8_t* out_shared) {
+  const int e = blockIdx.x;
+  if (e < count && hist && hist[e] == 0) return;  // expert without rows
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c16 = lane & 15;
+  const PackGeom geom = pack_geom(N, K, paired);
+  const int G = geom.G, q = blockIdx.y * 4 + wave;
+  if (q >= geom.n_wt * G) return;
+  const uint8_t* eb = e < count ? blob + (int64_t)e * expert_bytes : shared_blob;
+  uint8_t* ob = e < count ? out + (int64_t)e * geom.n_wt * G * kBf16GroupBytes : out_shared;
+  const uint8_t* nib = eb + geom.nib_off + ((int64_t)q * 128 + lane) * 16;
+  const u32x4 w0 = *reinterpret_cast<const u32x4*>(nib);
+  const u32x4 w1 = *reinterpret_cast<const u32x4*>(nib + 1024);
+  const u32x4 sbv = *reinterpret_cast<const u32x4*>(eb + geom.sb_off + ((int64_t)q * 16 + c16) * 16);
+  const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  const float sc[4] = {bf16lo(sbv.x), bf16hi(sbv.x), bf16lo(sbv.y), bf16hi(sbv.y)};
+  const float bi[4] = {bf16lo(sbv.z), bf16hi(sbv.z), bf16lo(sbv.w), bf16hi(sbv.w)};
+  const ExpandConsts xk = expand_consts();
+#pragma unroll
+  for (int wd = 0; wd < 8; ++wd) {
+    const int ct = wd >> 1;
+    const u32x4 v = expand_codes(words[wd], xk);
+    const uint32_t pr[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const float lo = __builtin_fmaf(bf16lo(pr[d]) - 128.0f, sc[ct], bi[ct]);
+      const float hi = __builtin_fmaf(bf16hi(pr[d]) - 128.0f, sc[ct], bi[ct]);
+      o[d] = (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+    }
+    *reinterpret_cast<u32x4*>(ob + ((int64_t)q * 8 + wd) * 1024 + lane * 16) = u32x4{o[0], o[1], o[2], o[3]};
+  }
+}
+
 // Test hook: expand one expert's packed matrices with the GEMM's own loads and
 // code expansion. Grid: (n_wt, G); block: 64 threads (one wave).
 __global__ void test_dequant_kernel(const uint8_t* ebase, int N, int K, int paired, float* out) {
@@ -623,24 +701,34 @@ int persistent_blocks() {
 }
 
 template <int MODE>
-hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_mode(const GemmArgs& a, hipStream_t s, int grid_blocks) {
+  if (a.bf16_weights) {
+    const int G = a.K / kGroup;
+    if (G % 2) return hipErrorInvalidValue;
+    const int exact = (grid_blocks + 7) / 8 * 8;
+    hipLaunchKernelGGL((gemm_ring_kernel<MODE, true>),
+                       dim3(grid_blocks > 0 ? exact : kRBlocksPerCU * persistent_blocks()),
+                       dim3(kRThreads), 0, s, a);
+    return hipGetLastError();
+  }
   const int G = a.K / kGroup;
   if (G < 2 || G > kMaxGroups) return hipErrorInvalidValue;
   const int cus = persistent_blocks();
+  const int exact = (grid_blocks + 7) / 8 * 8;
   if (G % kRS == 0) {
-    const dim3 grid(kRBlocksPerCU * cus), block(kRThreads);
-    hipLaunchKernelGGL(gemm_ring_kernel<MODE>, grid, block, 0, s, a);
+    const dim3 grid(grid_blocks > 0 ? exact : kRBlocksPerCU * cus), block(kRThreads);
+    hipLaunchKernelGGL((gemm_ring_kernel<MODE, false>), grid, block, 0, s, a);
     return hipGetLastError();
   }
-  const dim3 grid(cus), block(kThreads);
+  const dim3 grid(grid_blocks > 0 ? exact : cus), block(kThreads);
   hipLaunchKernelGGL((gemm_stream_kernel<MODE, 6>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t s) {
-  return mode == kGateUp ? launch_mode<kGateUp>(a, s) : launch_mode<kDown>(a, s);
+hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t s, int grid_blocks) {
+  return mode == kGateUp ? launch_mode<kGateUp>(a, s, grid_blocks) : launch_mode<kDown>(a, s, grid_blocks);
 }
 
 hipError_t launch_combine(const float* partial, const float* topk_w, uint16_t* y, int T, int N,
@@ -649,6 +737,16 @@ hipError_t launch_combine(const float* partial, const float* topk_w, uint16_t* y
   const int64_t threads = (int64_t)T * (N / 8);
   hipLaunchKernelGGL(combine_kernel<8>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
                      partial, topk_w, y, T, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_bf16(const uint8_t* blob, int64_t expert_bytes, const uint8_t* shared_blob,
+                              int count, const int32_t* hist, int N, int K, int paired, uint8_t* out,
+                              uint8_t* out_shared, hipStream_t s) {
+  const PackGeom g = pack_geom(N, K, paired);
+  const dim3 grid(count + 1, (g.n_wt * g.G + 3) / 4);
+  hipLaunchKernelGGL(expand_bf16_kernel, grid, dim3(256), 0, s, blob, expert_bytes, shared_blob, count,
+                     hist, N, K, paired, out, out_shared);
   return hipGetLastError();
 }
 

@@ -49,6 +49,7 @@ struct GemmArgs {
   const uint8_t* shared_blob;
   int64_t expert_bytes;
   int N, K, paired;          // packed geometry of this matrix set
+  int bf16_weights;          // 1: blob / shared_blob hold bf16-expanded weights (no header)
   int T;                     // tokens in this chunk
   int k;                     // experts per token
   // activations
@@ -64,10 +65,18 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* planes, float* parti
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_scan_scatter(const ScatterArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(int* p, int n, hipStream_t s);
-hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t s);
+// grid_blocks > 0: that many blocks (rounded up to a multiple of 8) instead
+// of the persistent grid (used when the host knows the exact unit count).
+hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t s, int grid_blocks = 0);
 // y[t][n] = bf16(partial[t][k][n] + sum_{j<k} topk_w[t][j] * partial[t][j][n]) (fixed order).
 hipError_t launch_combine(const float* partial, const float* topk_w, uint16_t* y, int T, int N,
                           int k, hipStream_t s);
+// The unfused comparison path: every expert of a packed blob with rows (hist
+// null or hist[e] > 0), and the shared expert, expanded to bf16 w = q s + b
+// (one rounding) into `out` / `out_shared` in the kBf16GroupBytes layout.
+hipError_t launch_expand_bf16(const uint8_t* blob, int64_t expert_bytes, const uint8_t* shared_blob,
+                              int count, const int32_t* hist, int N, int K, int paired, uint8_t* out,
+                              uint8_t* out_shared, hipStream_t s);
 hipError_t launch_test_dequant(const uint8_t* expert_base, int N, int K, int paired, float* out,
                                hipStream_t s);
 

@@ -38,6 +38,10 @@ constexpr int kGroup = 64;          // inputs per quantisation group
 constexpr int kWaveCols = 64;       // output columns per wave tile
 constexpr int kNibBytes = 2048;     // packed codes per (wave tile, group)
 constexpr int kSbBytes = 256;       // scales + biases per (wave tile, group)
+// The same weights expanded to bf16 (the unfused comparison path): per (wave
+// tile, group) 8 words x 64 lanes x 16 bytes, word w = 2 ct + ks holding the
+// B operand that code word w expands to.
+constexpr int kBf16GroupBytes = 8 * 64 * 16;
 constexpr int kHeaderBytes = 256;   // blob header
 constexpr uint32_t kMagic = 0x4734494Du;  // "MI4G"
 constexpr uint32_t kRouterMagic = 0x3346424Du;  // "MBF3"

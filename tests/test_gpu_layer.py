@@ -114,6 +114,41 @@ def test_prefill_t512_block16(torch_cuda):
     print(f"T=512 block_m 16: {s}")
 
 
+def test_prefill_host_routed_matches(torch_cuda):
+    # the host-synchronised routing variant launches exact grids; every unit
+    # is computed the same way, so y equals the GPU-routed call bit for bit
+    torch = torch_cuda
+    for name, T in (("prefill_t512", 512), ("skew_t2048", 2048), ("tiny_t32", 37)):
+        wl, w, dw = _layer(name)
+        x = synth.make_x(np.random.default_rng(T), T, w.H)
+        y_ref, _, _ = _prefill(torch, dw, x, route=False)
+        d = dw.dims
+        y = torch.empty((T, d.H), dtype=torch.int16, device="cuda")
+        B.moe_prefill_layer_host_routed(d, dw, torch.from_numpy(x).cuda(), y, T, 0,
+                                        B.workspace(d, T, B.MODE_PREFILL))
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy().view(np.uint16), y_ref), name
+
+
+def test_prefill_unfused_matches_oracle(torch_cuda):
+    # weights expanded to bf16 in memory, then the GEMMs on bf16 weights:
+    # the layer bar against the oracle still holds
+    torch = torch_cuda
+    for name, T in (("tiny_t32", 33), ("prefill_t512", 512)):
+        wl, w, dw = _layer(name)
+        x = synth.make_x(np.random.default_rng(T + 1), T, w.H)
+        d = dw.dims
+        y = torch.empty((T, d.H), dtype=torch.int16, device="cuda")
+        B.moe_prefill_layer_unfused(d, dw, torch.from_numpy(x).cuda(), y, T, B.unfused_weights(d),
+                                    ws=B.workspace(d, T, B.MODE_PREFILL))
+        y_ref, logits, meta = _prefill(torch, dw, x)
+        torch.cuda.synchronize()
+        y = y.cpu().numpy().view(np.uint16)
+        idx, wsel = _route_of(meta, T)
+        s = check_layer(x, w, y, logits, idx, wsel, tokens=np.arange(0, T, 3))
+        print(f"unfused {name} T={T}: {s}")
+
+
 def test_prefill_skew_t2048_sampled(torch_cuda):
     wl, w, dw = _layer("skew_t2048")
     _, _, x = synth.generate("skew_t2048", with_x=True)
