@@ -27,13 +27,15 @@ int n_chunks(const moe_dims* d, int T) {
   return (int)(((int64_t)d->top_k * T + kChunkPairs - 1) / kChunkPairs);
 }
 
-// Split the router's K dimension (at most kMaxSplits ways) so that the grid
-// has about 128..256 blocks.
-int router_splits(const moe_dims* d, int T) {
-  const int tiles = ((T + 63) / 64) * (d->E / 64);
+// Split the router's K dimension into the largest power of two <= kMaxSplits
+// that divides K / 64, whatever T is: the blocks stay short (each holds a
+// 72 KB LDS ring, so at most two run on a compute unit) and every logit is
+// the same fixed-order sum of the same partial sums for any chunking of the
+// tokens, so chunked and unchunked prompts get identical logits.
+int router_splits(const moe_dims* d, int /*T*/) {
   const int G = d->H / kGroup;
-  int s = 1;
-  while (s * 2 <= kMaxSplits && s * 2 * tiles <= 256 && s * 2 <= G && G % (s * 2) == 0) s *= 2;
+  int s = kMaxSplits;
+  while (G % s) s /= 2;
   return s;
 }
 
