@@ -16,8 +16,8 @@
 //                   for (unique expert or shared expert) x (64-column wave
 //                   tile); a token set that picks one expert twice shares its
 //                   read; block 0 also writes the routing metadata
-//   decode_down     per 64-column tile of the output: the down projection of
-//                   every (token, slot) pair, then
+//   decode_down     per token and 32-column half tile of the output: the
+//                   down projection of the token's (token, slot) pairs, then
 //                   y = bf16(shared + sum over the token's k slots of
 //                   weight * output) in a fixed order
 #include "kernels.h"
@@ -50,18 +50,27 @@ struct DecodeRoute {
   int n_uniq;
 };
 
-// Requires kDecThreads threads; every thread must call it.
-__device__ void decode_route(const DecodeArgs& a, DecodeRoute& r) {
+// This thread's four logits of token `wave` (waves >= T load token 0's and
+// do not use them): issued early so that their latency overlaps other work.
+__device__ inline void load_route_logits(const DecodeArgs& a, float (&lv)[4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* row = a.logits + (int64_t)(wave < a.T ? wave : 0) * a.E;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lv[i] = row[min(lane + 64 * i, a.E - 1)];
+}
+
+// Requires kDecThreads threads; every thread must call it, with the logits
+// from load_route_logits().
+__device__ void decode_route(const DecodeArgs& a, const float (&lv)[4], DecodeRoute& r) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, P = a.T * kK;
   if (wave < a.T) {
     const int t = wave;
-    const float* row = a.logits + (int64_t)t * E;
     uint32_t key[4];
     float val[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float v = i < E / 64 ? row[lane + 64 * i] : -INFINITY;
+      const float v = i < E / 64 ? lv[i] : -INFINITY;
       val[i] = v == v ? v : -INFINITY;  // a NaN logit ranks as -inf
       key[i] = i < E / 64 ? logit_key(val[i]) : 0u;
     }
@@ -207,8 +216,9 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
 // split K. Slot < k*T: the slot-th unique selected expert (blocks past the
 // number of unique experts exit); slot k*T: the shared expert. A half of a
 // 64-column wave tile is 16 gate and the matching 16 up columns. The
-// activations are loaded before the routing is recomputed and staged in LDS
-// after it; then each wave issues all of its groups' weight loads at once.
+// activations and the logits are loaded first; the activations are staged in
+// LDS while the logits are in flight; after the routing each wave issues all
+// of its groups' weight loads at once.
 template <int GPW>
 __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a) {
   __shared__ DecodeRoute r;
@@ -225,12 +235,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
   constexpr int kXPer = kDecodeMaxT * 4096 / 8 / kDecThreads;
 
   const int n16 = T * H / 8;
-  u32x4 xv[kXPer];  // (clamped, unconditional loads: no branches between them)
+  {
+    u32x4 xv[kXPer];  // (clamped, unconditional loads: no branches between them)
 #pragma unroll
-  for (int i = 0; i < kXPer; ++i)
-    xv[i] = reinterpret_cast<const u32x4*>(a.x)[min(tid + i * kDecThreads, n16 - 1)];
-
-  decode_route(a, r);
+    for (int i = 0; i < kXPer; ++i)
+      xv[i] = reinterpret_cast<const u32x4*>(a.x)[min(tid + i * kDecThreads, n16 - 1)];
+    float lv[4];
+    load_route_logits(a, lv);
+    // the activations go to LDS while the logits are still in flight
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i)
+      if (tid + i * kDecThreads < n16) xs_l[tid + i * kDecThreads] = xv[i];
+    decode_route(a, lv, r);  // its barriers also publish xs_l
+  }
 
   if (blockIdx.x == 0) {
     if (tid < P) {
@@ -287,10 +304,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
   }
   // keep every weight load ahead of the arithmetic (one memory round trip)
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < kXPer; ++i)
-    if (tid + i * kDecThreads < n16) xs_l[tid + i * kDecThreads] = xv[i];
-  __syncthreads();
 
   const ExpandConsts xk = expand_consts();
   float acc[kDecodeMaxT][2];
@@ -335,108 +348,101 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
   }
 }
 
-// Down projection and combine. Grid: H/64 column tiles x 2 halves of 32
-// columns; block: 8 waves.
-// Work is (token t, slot j) pairs, p = t (k+1) + j, slot k being the shared
-// expert, nine pairs at a time. Per batch of pairs and round of eight groups,
-// wave w takes group w of the round: the pairs' expert ids, then all their
-// weight loads and, at the same time, the block's copy of the pairs'
-// activation rows into LDS, one barrier, and the arithmetic; the column sums
-// of each pair stay in registers over the rounds. Then per pair
-// d[t][j] = sum over the eight waves in order, and
-// y[t] = bf16(d[t][k] + sum_{j<k} w[t][j] * d[t][j]), j ascending.
-constexpr int kDecPairs = kDecodeMaxT * (kK + 1);
-constexpr int kDecPairBatch = kK + 1;
+// Down projection and combine. Grid: T tokens x H/64 column tiles x 2 halves
+// of 32 columns; block: 8 waves. A block owns the k + 1 (token, slot) pairs
+// of its token, slot k being the shared expert. Per round of eight groups,
+// wave w takes group w of the round: all the pairs' weight loads and, at the
+// same time, the block's copy of the pairs' activation rows into LDS, one
+// barrier, and the arithmetic; the column sums of each pair stay in
+// registers over the rounds. The expert ids and routing weights are read
+// once, up front. Then per pair d[j] = sum over the eight waves in order, and
+// y[t] = bf16(d[k] + sum_{j<k} w[t][j] * d[j]), j ascending.
+constexpr int kDecPairs = kK + 1;
 
 __global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs a) {
   __shared__ float red[kDecWaves][kDecPairs][kWaveCols / 2];
-  __shared__ u32x4 hs[kDecPairBatch][kDecWaves * kGroup / 8];  // [pair][group in round][8 inputs]
+  __shared__ u32x4 hs[kDecPairs][kDecWaves * kGroup / 8];  // [pair][group in round][8 inputs]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kb = lane >> 4;
   const int T = a.T, H = a.H, I = a.I;
   const PackGeom geom = pack_geom(H, I, 0);
-  const int wt = blockIdx.x >> 1, half = blockIdx.x & 1, G = geom.G;
-  const int n_pairs = (kK + 1) * T;
+  const int half = blockIdx.x & 1, wt = (blockIdx.x >> 1) % geom.n_wt;
+  const int t = (blockIdx.x >> 1) / geom.n_wt, G = geom.G;
   const ExpandConsts xk = expand_consts();
-  for (int p0 = 0; p0 < n_pairs; p0 += kDecPairBatch) {
-    const int nb = min(kDecPairBatch, n_pairs - p0);
-    int ex[kDecPairBatch];
+  int ex[kDecPairs];
+  float wj[kK];
 #pragma unroll
-    for (int b = 0; b < kDecPairBatch; ++b) {
-      const int p = min(p0 + b, n_pairs - 1), t = p / (kK + 1), j = p % (kK + 1);
-      ex[b] = j < kK ? a.topk_idx[t * kK + j] : -1;  // -1: the shared expert
+  for (int j = 0; j < kK; ++j) {
+    ex[j] = a.topk_idx[t * kK + j];
+    wj[j] = a.topk_w[t * kK + j];
+  }
+  ex[kK] = -1;  // the shared expert
+  float acc[kDecPairs][2];
+#pragma unroll
+  for (int j = 0; j < kDecPairs; ++j) acc[j][0] = acc[j][1] = 0.f;
+  for (int r0 = 0; r0 < G; r0 += kDecWaves) {
+    const int ng = min(kDecWaves, G - r0), g = r0 + wave;
+    static_assert(kDecWaves * kGroup / 8 == 64, "LDS row of the round: 64 chunks of 8 inputs");
+    // activation rows of this round (independent of the expert ids)
+    constexpr int kHsPer = (kDecPairs * kDecWaves * kGroup / 8 + kDecThreads - 1) / kDecThreads;
+    // (unconditional, clamped loads: no branches between the loads)
+    u32x4 hv[kHsPer];
+#pragma unroll
+    for (int q = 0; q < kHsPer; ++q) {
+      const int i = tid + q * kDecThreads;
+      const int j = min(i >> 6, kDecPairs - 1), c = min(i & 63, 8 * ng - 1);
+      const int row = j < kK ? t * kK + j : kK * T + t;
+      hv[q] = *reinterpret_cast<const u32x4*>(a.h + (int64_t)row * I + r0 * kGroup + 8 * c);
     }
-    float acc[kDecPairBatch][2];
+    u32x4 wq[kDecPairs], sb[kDecPairs];
+    const int gl = min(g, G - 1);  // waves past G load group G - 1 and do not use it
 #pragma unroll
-    for (int b = 0; b < kDecPairBatch; ++b) acc[b][0] = acc[b][1] = 0.f;
-    for (int r0 = 0; r0 < G; r0 += kDecWaves) {
-      const int ng = min(kDecWaves, G - r0), g = r0 + wave;
-      static_assert(kDecWaves * kGroup / 8 == 64, "LDS row of the round: 64 chunks of 8 inputs");
-      // activation rows of this batch and round (independent of the expert ids)
-      constexpr int kHsPer = (kDecPairBatch * kDecWaves * kGroup / 8 + kDecThreads - 1) / kDecThreads;
-      // (unconditional, clamped loads: no branches between the loads)
-      u32x4 hv[kHsPer];
-#pragma unroll
-      for (int q = 0; q < kHsPer; ++q) {
-        const int i = tid + q * kDecThreads;
-        const int b = min(i >> 6, nb - 1), c = min(i & 63, 8 * ng - 1), p = p0 + b;
-        const int t = p / (kK + 1), j = p % (kK + 1);
-        const int row = j < kK ? t * kK + j : kK * T + t;
-        hv[q] = *reinterpret_cast<const u32x4*>(a.h + (int64_t)row * I + r0 * kGroup + 8 * c);
-      }
-      u32x4 wq[kDecPairBatch], sb[kDecPairBatch];
-      const int gl = min(g, G - 1);  // waves past G load group G - 1 and do not use it
-#pragma unroll
-      for (int b = 0; b < kDecPairBatch; ++b) {
-        const int e = __builtin_amdgcn_readfirstlane(ex[b]);
-        const uint8_t* eb = e >= 0 ? a.dn_blob + (int64_t)e * a.dn_expert_bytes : a.dn_shared;
-        wq[b] = *reinterpret_cast<const u32x4*>(eb + geom.nib_off +
-                                                (((int64_t)wt * G + gl) * 128 + 64 * half + lane) * 16);
-        sb[b] = *reinterpret_cast<const u32x4*>(eb + geom.sb_off + (((int64_t)wt * G + gl) * 16 + c16) * 16);
-      }
-      // keep every load of the batch ahead of the LDS copy and the arithmetic
-      __builtin_amdgcn_sched_barrier(0);
-      if (p0 > 0 || r0 > 0) __syncthreads();  // every wave is done with the previous rows
-#pragma unroll
-      for (int q = 0; q < kHsPer; ++q) {
-        const int i = tid + q * kDecThreads;
-        if ((i >> 6) < nb && (i & 63) < 8 * ng) hs[i >> 6][i & 63] = hv[q];
-      }
-      __syncthreads();
-      if (g < G) {
-        const int c = 8 * wave + kb;
-#pragma unroll
-        for (int b = 0; b < kDecPairBatch; ++b)
-          if (b < nb) gemv_half(wq[b], sb[b], half, hs[b][c], hs[b][c + 4], xk, acc[b]);
-      }
+    for (int j = 0; j < kDecPairs; ++j) {
+      const int e = __builtin_amdgcn_readfirstlane(ex[j]);
+      const uint8_t* eb = e >= 0 ? a.dn_blob + (int64_t)e * a.dn_expert_bytes : a.dn_shared;
+      wq[j] = *reinterpret_cast<const u32x4*>(eb + geom.nib_off +
+                                              (((int64_t)wt * G + gl) * 128 + 64 * half + lane) * 16);
+      sb[j] = *reinterpret_cast<const u32x4*>(eb + geom.sb_off + (((int64_t)wt * G + gl) * 16 + c16) * 16);
     }
+    // keep every load of the round ahead of the LDS copy and the arithmetic
+    __builtin_amdgcn_sched_barrier(0);
+    if (r0 > 0) __syncthreads();  // every wave is done with the previous rows
 #pragma unroll
-    for (int b = 0; b < kDecPairBatch; ++b) {
-      if (b < nb) {
+    for (int q = 0; q < kHsPer; ++q) {
+      const int i = tid + q * kDecThreads;
+      if ((i >> 6) < kDecPairs && (i & 63) < 8 * ng) hs[i >> 6][i & 63] = hv[q];
+    }
+    __syncthreads();
+    if (g < G) {
+      const int c = 8 * wave + kb;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          float v = acc[b][c];
-          v += __shfl_xor(v, 16);
-          v += __shfl_xor(v, 32);
-          if (kb == 0) red[wave][p0 + b][16 * c + c16] = v;
-        }
-      }
+      for (int j = 0; j < kDecPairs; ++j) gemv_half(wq[j], sb[j], half, hs[j][c], hs[j][c + 4], xk, acc[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kDecPairs; ++j) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float v = acc[j][c];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (kb == 0) red[wave][j][16 * c + c16] = v;
     }
   }
   __syncthreads();
-  if (tid < T * kWaveCols / 2) {
-    const int t = tid / (kWaveCols / 2), n = tid % (kWaveCols / 2);
+  if (tid < kWaveCols / 2) {
+    const int n = tid;
     float d[kK + 1];
 #pragma unroll
     for (int j = 0; j <= kK; ++j) {
       float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) v += red[w][t * (kK + 1) + j][n];
+      for (int w = 0; w < kDecWaves; ++w) v += red[w][j][n];
       d[j] = v;
     }
     float s = d[kK];
 #pragma unroll
-    for (int j = 0; j < kK; ++j) s = __builtin_fmaf(a.topk_w[t * kK + j], d[j], s);
+    for (int j = 0; j < kK; ++j) s = __builtin_fmaf(wj[j], d[j], s);
     a.y[(int64_t)t * H + 64 * wt + 32 * half + n] = f2bf(s);
   }
 }
@@ -472,7 +478,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return e;
   if ((e = launch_gateup(gu.G, dim3(slots * gu.n_wt * 2), s, a)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_down_kernel, dim3(dn.n_wt * 2), dim3(kDecThreads), 0, s, a);
+  hipLaunchKernelGGL(decode_down_kernel, dim3(a.T * dn.n_wt * 2), dim3(kDecThreads), 0, s, a);
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return e;
   return hipGetLastError();
 }
