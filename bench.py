@@ -17,6 +17,9 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   roofline      the dominant kernel (gate/up GEMM): algorithmic bytes or
                 flops per launch / its mean duration from HIP events recorded
                 on the library's stream around every launch in the timed region
+                (plus that rate over the measured ceiling below)
+  ceilings      measured on this device in the same run: streaming HBM read
+                GB/s over a 2 GiB buffer and the bf16 MFMA loop's TFLOP/s
   cpu_baseline  the CPU oracle timed on this host on the same workload
   secondary     the 2048-token Zipf-skewed prefill (bf16 MFMA fraction), the
                 16384-token prompt in 4096-token chunks, and batch-1 and
@@ -245,6 +248,40 @@ def cpu_baseline(w, x, min_seconds=10.0):
             f"{dt:.1f} s wall"}
 
 
+def measure_ceilings(read_bytes=2 << 30, mfma_iters=4000, reps=5):
+    """Achievable HBM read bandwidth and bf16 MFMA rate on this device, from the
+    library's measurement kernels (a streaming read of a buffer 8x the 256 MB
+    last-level cache; independent 16x16x32 bf16 MFMA chains), best of `reps`."""
+    import torch
+    from int4_grouped_gemm_router_amd import binding as B
+    buf = torch.empty(read_bytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+
+    def best(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts)
+
+    t_read = best(lambda: B.moe_ceiling_read(buf, sink))
+    flops = [0.0]
+
+    def mfma():
+        flops[0] = B.moe_ceiling_mfma(mfma_iters, sink)
+
+    t_mfma = best(mfma)
+    del buf
+    return {"hbm_read_gbs": read_bytes / t_read / 1e9, "read_bytes": read_bytes,
+            "mfma_bf16_tflops": flops[0] / t_mfma / 1e12, "mfma_flops": flops[0],
+            "method": "moe_ceiling_read / moe_ceiling_mfma, best of %d event-timed launches" % reps}
+
+
 def measured_traffic(workload):
     """HBM bytes per gate/up launch from the committed FETCH_SIZE / WRITE_SIZE
     summary, or None when it is missing, for another workload, or taken from
@@ -390,6 +427,11 @@ def main():
                     "unit": "TFLOP/s", "frac": res["gateup_tflops"] / PEAK_BF16_TFLOPS,
                     "traffic": None, "kernel": "gemm_gateup", "mean_us": gu_us}
     roofline["dominant_kernel"] = dominant
+    ceil = measure_ceilings()
+    log(f"measured ceilings: {ceil}")
+    roofline["measured_peak"] = (ceil["hbm_read_gbs"] if roofline["unit"] == "GB/s"
+                                 else ceil["mfma_bf16_tflops"])
+    roofline["frac_of_measured"] = roofline["achieved"] / roofline["measured_peak"]
     out = {
         "metric": METRIC, "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
@@ -402,6 +444,7 @@ def main():
                    "block_m": args.block_m,
                    "parallelism": "single GPU"},
         "roofline": roofline,
+        "ceilings": ceil,
         "kernels_us": res["kernels_us"],
         "expert_tflops": res["expert_tflops"],
         "mfma_frac_layer": res["mfma_frac_layer"],
@@ -423,6 +466,11 @@ def main():
         r5 = run_decode("decode_t4", args.decode_steps, 20, 32)
         log(f"decode_t4: {r5}")
         sec.append(r5)
+        for r in sec:
+            if "expert_tflops" in r:
+                r["mfma_frac_of_measured"] = r["expert_tflops"] / ceil["mfma_bf16_tflops"]
+            if "gemv_gbs" in r:
+                r["hbm_frac_of_measured"] = r["gemv_gbs"] / ceil["hbm_read_gbs"]
         out["secondary"] = sec
     print(json.dumps(out), flush=True)
 

@@ -223,6 +223,27 @@ const char* moe_strerror(int code);
 int moe_test_dequant(const void* blob, int32_t count, int32_t N, int32_t K, int32_t paired,
                      int32_t expert, float* out, void* stream);
 
+/* Measurement helpers, not part of the layer: achievable ceilings of the
+ * device, for roofline fractions against measured as well as published peaks.
+ *
+ * moe_ceiling_read enqueues one streaming read of `bytes` (a multiple of 16,
+ * >= 16) of device memory at `buf` by 2048 blocks of 256 threads, each block
+ * one contiguous 1/2048 of the buffer (16-byte vector loads, eight in flight
+ * per thread). `sink` (device, 4 bytes) is
+ * written only if the XOR of a thread's data equals a fixed constant, which
+ * keeps the loads live; callers ignore its value. Time it with events; for
+ * HBM bandwidth use a buffer much larger than the 256 MB last-level cache.
+ *
+ * moe_ceiling_mfma enqueues 1024 blocks of four waves, each wave running
+ * eight independent chains of `iters` 16x16x32 bf16 matrix-core operations
+ * on register operands, and stores the flop count of the launch in *flops
+ * (host). `sink` as above.
+ *
+ * Both return MOE_EINVAL for null pointers or bad sizes, MOE_EHIP if the
+ * launch fails; they allocate nothing and do not synchronise. */
+int moe_ceiling_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+int moe_ceiling_mfma(int32_t iters, float* sink, double* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

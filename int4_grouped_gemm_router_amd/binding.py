@@ -89,6 +89,8 @@ def lib():
         L.moe_prefill_layer_unfused.argtypes = [P(MoeDims), P(MoeLayerWeights), _vp, _vp, _i32, _i32,
                                                 _vp, _sz, _vp, _sz, _vp]
         L.moe_decode_layer_profiled.argtypes = L.moe_decode_layer.argtypes + [_vp, _i32]
+        L.moe_ceiling_read.argtypes = [_vp, _sz, _vp, _vp]
+        L.moe_ceiling_mfma.argtypes = [_i32, _vp, P(ctypes.c_double), _vp]
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
         L.moe_test_dequant.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp]
@@ -96,7 +98,7 @@ def lib():
                      "moe_prefill_layer", "moe_decode_layer", "moe_test_dequant",
                      "moe_prefill_layer_profiled", "moe_decode_layer_profiled",
                      "moe_prefill_layer_host_routed", "moe_unfused_weight_bytes",
-                     "moe_prefill_layer_unfused"):
+                     "moe_prefill_layer_unfused", "moe_ceiling_read", "moe_ceiling_mfma"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -348,6 +350,20 @@ def moe_decode_layer_profiled(d: MoeDims, w: DeviceWeights, x, y, T: int, events
                                            0 if ws is None else ws.numel(), _stream(stream),
                                            ctypes.cast(arr, _vp), len(arr)),
            "moe_decode_layer_profiled")
+
+
+def moe_ceiling_read(buf, sink, stream=None):
+    """Enqueue one streaming read of the device buffer `buf` (measurement helper)."""
+    _check(lib().moe_ceiling_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                  _stream(stream)), "moe_ceiling_read")
+
+
+def moe_ceiling_mfma(iters: int, sink, stream=None) -> float:
+    """Enqueue the bf16 matrix-core loop; returns the launch's flop count."""
+    flops = ctypes.c_double(0.0)
+    _check(lib().moe_ceiling_mfma(iters, _ptr(sink), ctypes.byref(flops), _stream(stream)),
+           "moe_ceiling_mfma")
+    return flops.value
 
 
 def moe_test_dequant(blob, count, N, K, paired, expert, out, stream=None):

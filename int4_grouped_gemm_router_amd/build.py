@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libmoe_int4.so")
-SOURCES = ["abi.hip", "route.hip", "gemm.hip", "decode.hip", "pack.hip"]
+SOURCES = ["abi.hip", "route.hip", "gemm.hip", "decode.hip", "pack.hip", "ceiling.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -27,9 +27,14 @@ FLAGS = [
 ]
 
 
+# per-source additions: the ceiling loop keeps its accumulators in VGPRs (the
+# default AGPR assignment shuffles them between register files every step)
+EXTRA_FLAGS = {"ceiling.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -17,6 +17,13 @@ Commands (run from the repository root):
       by the factors the copy dispatches give, as HBM bytes per launch. The
       result records a digest of the kernel's sources; bench.py reports the
       traffic only while the sources still match it.
+
+  python3 -m int4_grouped_gemm_router_amd.profiling counters --dir DIR [--dir DIR ...] \
+        --command ... --out FILE
+      Mean value per dispatch of every counter collected by one or more
+      `rocprofv3 --pmc ... -d DIR -o run` passes, per kernel of the layer (the
+      ceiling measurement kernels are left out), with a few derived figures (matrix-core busy share, bf16 TFLOP/s from
+      the MFMA op count, VALU instructions per MFMA, L2 hit rate).
 """
 from __future__ import annotations
 
@@ -122,6 +129,62 @@ def traffic(a):
     print(json.dumps(res, indent=1))
 
 
+N_SIMDS = 256 * 4  # compute units x SIMDs of one MI355X
+N_XCDS = 8
+
+
+def counters(dirs, commands, out, match="moe::", skip="ceiling_"):
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    durs = collections.defaultdict(list)
+    for d in dirs:
+        seen = set()
+        for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+            k = r["Kernel_Name"]
+            if match not in k or skip in k:  # the layer's kernels, not the measurement helpers
+                continue
+            vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            key = (d, r["Dispatch_Id"])
+            if key not in seen:
+                seen.add(key)
+                durs[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    lines = ["# rocprofv3 hardware counters, mean per dispatch", "# commands:"]
+    lines += [f"#   {c}" for c in commands]
+    lines += ["# derived (MI355X: 1024 SIMDs in 8 XCDs; GRBM_GUI_ACTIVE reads the sum over the XCDs):",
+              "#   mfma_busy  = SQ_VALU_MFMA_BUSY_CYCLES / (1024 * GRBM_GUI_ACTIVE / 8)",
+              "#   bf16_tflops = 512 * SQ_INSTS_VALU_MFMA_MOPS_BF16 / dispatch duration (counter run)",
+              "#   valu_per_mfma = SQ_INSTS_VALU / SQ_INSTS_MFMA",
+              "#   valu_issue = 4 * SQ_ACTIVE_INST_VALU / (1024 * GRBM_GUI_ACTIVE / 8)",
+              "#   wave_wait = SQ_WAIT_ANY / SQ_WAVE_CYCLES, l2_hit = TCC_HIT / (TCC_HIT + TCC_MISS)", ""]
+    for k in sorted(vals, key=lambda k: -max(durs[k]) if durs[k] else 0):
+        m = {c: sum(v) / len(v) for c, v in vals[k].items()}
+        dur = sum(durs[k]) / len(durs[k])
+        name = k if len(k) <= 70 else k[:67] + "..."
+        lines.append(f"{name}  (mean dispatch {dur * 1e6:.1f} us in the counter runs)")
+        for c in sorted(m):
+            lines.append(f"    {c:<34s} {m[c]:>16.0f}")
+        cyc = m.get("GRBM_GUI_ACTIVE", 0.0) / N_XCDS
+        der = []
+        if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            der.append(f"mfma_busy {m['SQ_VALU_MFMA_BUSY_CYCLES'] / (N_SIMDS * cyc):.3f}")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in m and dur > 0:
+            der.append(f"bf16_tflops {512 * m['SQ_INSTS_VALU_MFMA_MOPS_BF16'] / dur / 1e12:.1f}")
+        if m.get("SQ_INSTS_MFMA"):
+            der.append(f"valu_per_mfma {m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f}")
+        if cyc and "SQ_ACTIVE_INST_VALU" in m:
+            der.append(f"valu_issue {4 * m['SQ_ACTIVE_INST_VALU'] / (N_SIMDS * cyc):.3f}")
+        if m.get("SQ_WAVE_CYCLES") and "SQ_WAIT_ANY" in m:
+            der.append(f"wave_wait {m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.3f}")
+        if "TCC_HIT_sum" in m and "TCC_MISS_sum" in m and m["TCC_HIT_sum"] + m["TCC_MISS_sum"] > 0:
+            der.append(f"l2_hit {m['TCC_HIT_sum'] / (m['TCC_HIT_sum'] + m['TCC_MISS_sum']):.3f}")
+        if der:
+            lines.append("    derived: " + ", ".join(der))
+        lines.append("")
+    text = "\n".join(lines)
+    with open(out, "w") as f:
+        f.write(text)
+    print(text)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -135,11 +198,17 @@ def main(argv=None):
         t.add_argument("--" + n.replace("_", "-"), dest=n, required=True)
     t.add_argument("--grid", type=int, default=None)
     t.add_argument("--command", action="append", default=[])
+    c = sub.add_parser("counters")
+    c.add_argument("--dir", action="append", required=True)
+    c.add_argument("--command", action="append", default=[])
+    c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "copy":
         run_copy()
     elif a.cmd == "kernel-stats":
         kernel_stats(a.dir, a.command, a.out)
+    elif a.cmd == "counters":
+        counters(a.dir, a.command, a.out)
     else:
         traffic(a)
 

@@ -294,3 +294,19 @@ def test_prefill_graph_replay_matches_eager(torch_cuda):
         B.moe_prefill_layer(d, dw, xd, y, T, 0, None, None, ws)   # eager work in between
         torch.cuda.synchronize()
         assert torch.equal(y, y_eager)
+
+
+@pytest.mark.gpu
+def test_ceiling_helpers_run():
+    """The measurement kernels launch through the C ABI, finish, and leave the
+    sink untouched (their conditional store never fires on these inputs)."""
+    import torch
+    buf = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    B.moe_ceiling_read(buf, sink)
+    flops = B.moe_ceiling_mfma(8, sink)
+    torch.cuda.synchronize()
+    assert flops == 1024 * 4 * 8 * 8 * (16 * 16 * 32 * 2)
+    assert torch.count_nonzero(sink).item() == 0
+    with pytest.raises(B.MoeError):
+        B.moe_ceiling_read(buf[:15], sink)  # not a multiple of 16 bytes
