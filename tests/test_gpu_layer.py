@@ -261,6 +261,32 @@ def test_decode_tiny_and_vs_prefill(torch_cuda):
         assert_y_close(synth.bf16_bits_to_f32(yd), synth.bf16_bits_to_f32(yp), "decode vs prefill")
 
 
+# Other sizes of the same layer family, chosen to reach the paths the main
+# shapes do not: (1024, 384, E=128): gate/up over 16 groups, down over K = 384
+# (6 groups, the LDS-stream GEMM); (4096, 256, E=64): gate/up over 64 groups
+# (the most the GEMMs and the decode kernels take), down over 4 groups;
+# (768, 640, E=192): 12 and 10 groups. Prefill on a ragged 40-token batch,
+# then decode at T = 1 and 4.
+@pytest.mark.parametrize("H,I,E", [(1024, 384, 128), (4096, 256, 64), (768, 640, 192)])
+def test_other_family_sizes(torch_cuda, H, I, E):
+    rng = np.random.default_rng(H + I + E)
+    w = synth.make_weights(rng, H, I, E)
+    dw = B.DeviceWeights.from_logical(w)
+    x = synth.make_x(rng, 40, H)
+    y, logits, meta = _prefill(torch_cuda, dw, x)
+    idx, wsel = _route_of(meta, 40)
+    s = check_layer(x, w, y, logits, idx, wsel)
+    check_route_meta(meta, idx, E, 8, 32)
+    print(f"prefill H={H} I={I} E={E}: {s}")
+    for T in (1, 4):
+        xt = synth.make_x(rng, T, H)
+        yd, ld, md = _decode(torch_cuda, dw, xt)
+        idx, wsel = _route_of(md, T)
+        s = check_layer(xt, w, yd, ld, idx, wsel)
+        check_route_meta(md, idx, E, 8, 32)
+        print(f"decode T={T} H={H} I={I} E={E}: {s}")
+
+
 def test_prefill_graph_replay_matches_eager(torch_cuda):
     """The layer captured in a HIP graph and replayed (with eager work and
     synchronisations in between) gives exactly the eager output every time."""
