@@ -28,6 +28,8 @@
 // output in fp32 at [token][slot]; the combine kernel then forms
 // y = bf16(shared + sum over the k slots of weight * output) in a fixed order,
 // so the result is deterministic.
+#include <atomic>
+
 #include "kernels.h"
 
 namespace moe {
@@ -685,19 +687,23 @@ __global__ void test_dequant_kernel(const uint8_t* ebase, int N, int K, int pair
 
 namespace {
 
-// Persistent grid: one block per compute unit (a multiple of 8 for the XCD mapping).
+// Persistent grid: one block per compute unit (a multiple of 8 for the XCD
+// mapping). The per-device count is cached; concurrent first calls may both
+// query it and store the same value (relaxed atomics, no lock needed).
 int persistent_blocks() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (!v) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 8)
       cus = 256;
-    cached[dev] = cus / 8 * 8;
+    v = cus / 8 * 8;
+    cached[dev].store(v, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return v;
 }
 
 template <int MODE>
