@@ -212,24 +212,33 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeArgs a) {
   }
 }
 
-// Grid: (k*T + 1) slots x n_wt wave tiles x 2 halves; block: 8 waves that
-// split K. Slot < k*T: the slot-th unique selected expert (blocks past the
-// number of unique experts exit); slot k*T: the shared expert. A half of a
-// 64-column wave tile is 16 gate and the matching 16 up columns. The
-// activations and the logits are loaded first; the activations are staged in
-// LDS while the logits are in flight; after the routing each wave issues all
-// of its groups' weight loads at once.
-template <int GPW>
+// Grid: (k*T + 1) slots x n_wt wave tiles x 2 / NH halves; block: 8 waves
+// that split K. Slot k*T: the shared expert (the first blocks of the grid);
+// slot < k*T: the slot-th unique selected expert (blocks past the number of
+// unique experts exit). A half of
+// a 64-column wave tile is 16 gate and the matching 16 up columns; a block
+// takes NH halves: one at a single token (twice the blocks to spread 16 MB
+// over the chip), both from two tokens on (half the blocks, so that every
+// block of a step is resident at once and no second round of blocks pays the
+// logits -> top-k -> weights latency chain again). The activations and the
+// logits are loaded first; the activations are staged in LDS while the
+// logits are in flight; after the routing each wave issues all of its
+// groups' weight loads at once.
+template <int GPW, int NH>
 __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a) {
   __shared__ DecodeRoute r;
-  __shared__ float red[kDecWaves][kDecodeMaxT][kWaveCols / 2];
+  __shared__ float red[kDecWaves][kDecodeMaxT][NH][kWaveCols / 2];
   __shared__ u32x4 xs_l[kDecodeMaxT * 4096 / 8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kb = lane >> 4;
   const int T = a.T, P = T * kK, H = a.H, I = a.I;
   const PackGeom geom = pack_geom(I, H, 1);
-  const int half = blockIdx.x & 1;
-  const int slot = (blockIdx.x >> 1) / geom.n_wt, wt = (blockIdx.x >> 1) % geom.n_wt;
+  const int half0 = NH == 2 ? 0 : blockIdx.x & 1;  // first half of the block
+  const int tile = NH == 2 ? blockIdx.x : blockIdx.x >> 1;
+  // the shared expert's tiles first, then the unique routed experts in
+  // order: blocks past the unique experts (which exit at once) come last
+  const int sraw = tile / geom.n_wt, wt = tile % geom.n_wt;
+  const int slot = sraw == 0 ? P : sraw - 1;
   const int G = geom.G;
   constexpr int gpw = GPW;  // groups per wave (G <= kDecWaves * GPW)
   constexpr int kXPer = kDecodeMaxT * 4096 / 8 / kDecThreads;
@@ -294,21 +303,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
 
   // (unconditional loads, groups past G clamped to G - 1 and not used: no
   // branches between the loads)
-  u32x4 wq[GPW], sb[GPW];
+  // (one scale/bias record serves both halves)
+  u32x4 wq[GPW][NH], sb[GPW];
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     const int g = min(wave * gpw + gi, G - 1);
-    wq[gi] = *reinterpret_cast<const u32x4*>(ebase + geom.nib_off +
-                                             (((int64_t)wt * G + g) * 128 + 64 * half + lane) * 16);
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh)
+      wq[gi][hh] = *reinterpret_cast<const u32x4*>(
+          ebase + geom.nib_off + (((int64_t)wt * G + g) * 128 + 64 * (half0 + hh) + lane) * 16);
     sb[gi] = *reinterpret_cast<const u32x4*>(ebase + geom.sb_off + (((int64_t)wt * G + g) * 16 + c16) * 16);
   }
   // keep every weight load ahead of the arithmetic (one memory round trip)
   __builtin_amdgcn_sched_barrier(0);
 
   const ExpandConsts xk = expand_consts();
-  float acc[kDecodeMaxT][2];
+  float acc[kDecodeMaxT][NH][2];
 #pragma unroll
-  for (int t = 0; t < kDecodeMaxT; ++t) acc[t][0] = acc[t][1] = 0.f;
+  for (int t = 0; t < kDecodeMaxT; ++t)
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) acc[t][hh][0] = acc[t][hh][1] = 0.f;
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     const int g = wave * gpw + gi;
@@ -317,7 +331,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
       for (int t = 0; t < kDecodeMaxT; ++t) {
         if (t < T && jslot[t] >= 0) {
           const int base16 = (t * H + g * kGroup + 8 * kb) / 8;
-          gemv_half(wq[gi], sb[gi], half, xs_l[base16], xs_l[base16 + 4], xk, acc[t]);
+#pragma unroll
+          for (int hh = 0; hh < NH; ++hh)
+            gemv_half(wq[gi][hh], sb[gi], half0 + hh, xs_l[base16], xs_l[base16 + 4], xk, acc[t][hh]);
         }
       }
     }
@@ -325,25 +341,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
 #pragma unroll
   for (int t = 0; t < kDecodeMaxT; ++t)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      if (t < T) {
-        float v = acc[t][c];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        if (kb == 0) red[wave][t][16 * c + c16] = v;  // c = 0: gate, c = 1: up
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if (t < T) {
+          float v = acc[t][hh][c];
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 32);
+          if (kb == 0) red[wave][t][hh][16 * c + c16] = v;  // c = 0: gate, c = 1: up
+        }
       }
-    }
   __syncthreads();
-  if (tid < T * 16) {
-    const int t = tid / 16, j = tid % 16;
+  if (tid < T * 16 * NH) {
+    const int t = tid / (16 * NH), hh = (tid / 16) % NH, j = tid % 16;
     if (jslot[t] >= 0) {
       float gv = 0.f, uv = 0.f;
       for (int w = 0; w < kDecWaves; ++w) {
-        gv += red[w][t][j];
-        uv += red[w][t][16 + j];
+        gv += red[w][t][hh][j];
+        uv += red[w][t][hh][16 + j];
       }
       const int row = jslot[t] == kK ? kK * T + t : t * kK + jslot[t];
-      a.h[(int64_t)row * I + 32 * wt + 16 * half + j] = f2bf(silu(gv) * uv);
+      a.h[(int64_t)row * I + 32 * wt + 16 * (half0 + hh) + j] = f2bf(silu(gv) * uv);
     }
   }
 }
@@ -450,18 +468,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs a) 
 namespace {
 
 // Smallest groups-per-wave instantiation that covers G groups with 8 waves.
-hipError_t launch_gateup(int G, dim3 grid, hipStream_t s, const DecodeArgs& a) {
+template <int NH>
+hipError_t launch_gateup_nh(int G, dim3 grid, hipStream_t s, const DecodeArgs& a) {
   if (G <= kDecWaves)
-    hipLaunchKernelGGL(decode_gateup_kernel<1>, grid, dim3(kDecThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_gateup_kernel<1, NH>), grid, dim3(kDecThreads), 0, s, a);
   else if (G <= 2 * kDecWaves)
-    hipLaunchKernelGGL(decode_gateup_kernel<2>, grid, dim3(kDecThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_gateup_kernel<2, NH>), grid, dim3(kDecThreads), 0, s, a);
   else if (G <= 4 * kDecWaves)
-    hipLaunchKernelGGL(decode_gateup_kernel<4>, grid, dim3(kDecThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_gateup_kernel<4, NH>), grid, dim3(kDecThreads), 0, s, a);
   else if (G <= 8 * kDecWaves)
-    hipLaunchKernelGGL(decode_gateup_kernel<8>, grid, dim3(kDecThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_gateup_kernel<8, NH>), grid, dim3(kDecThreads), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipSuccess;
+}
+
+// Half-tile blocks at one token, whole wave tiles from two tokens on.
+hipError_t launch_gateup(int G, int slots, int n_wt, int T, hipStream_t s, const DecodeArgs& a) {
+  if (T == 1) return launch_gateup_nh<1>(G, dim3(slots * n_wt * 2), s, a);
+  return launch_gateup_nh<2>(G, dim3(slots * n_wt), s, a);
 }
 
 }  // namespace
@@ -476,7 +501,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return e;
   hipLaunchKernelGGL(decode_router_kernel, dim3(a.E), dim3(256), 0, s, a);
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return e;
-  if ((e = launch_gateup(gu.G, dim3(slots * gu.n_wt * 2), s, a)) != hipSuccess) return e;
+  if ((e = launch_gateup(gu.G, slots, gu.n_wt, a.T, s, a)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return e;
   hipLaunchKernelGGL(decode_down_kernel, dim3(a.T * dn.n_wt * 2), dim3(kDecThreads), 0, s, a);
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return e;
