@@ -149,9 +149,10 @@ int moe_route(const moe_dims* dims, const float* logits, int32_t T, const moe_ro
  * non-null, receives the routing metadata of the LAST chunk (sized for that
  * chunk's token count). Numerics: fp32 router logits; int4 codes are expanded
  * exactly to bf16 on chip, scale and bias applied in fp32; fp32 accumulation;
- * the SwiGLU product h is rounded to bf16 before the down projection; the
- * k routed outputs and the shared output are summed in fp32; y is rounded
- * once to bf16. T = 0 is a no-op. */
+ * the SwiGLU product h is rounded to bf16 before the down projection; each
+ * of the k routed down outputs is rounded to bf16 (it enters with a routing
+ * weight of about 1/k), the shared expert's stays fp32, and they are summed
+ * in fp32 in a fixed order; y is rounded once to bf16. T = 0 is a no-op. */
 int moe_prefill_layer(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x,
                       uint16_t* y, int32_t T, int32_t chunk_T, float* logits_out,
                       const moe_route_out* route_out, void* ws, size_t ws_bytes, void* stream);

@@ -57,7 +57,8 @@ struct PrefillWs {
   int32_t *items, *num_items;
   float* topk_w;
   uint16_t* h;  // [(k+1)Tc][I]
-  float* partial;
+  uint16_t* partial_r;  // routed down rows, bf16 [k*Tc][H]
+  float* partial_s;     // shared-expert down rows, fp32 [Tc][H]
 };
 
 PrefillWs carve_prefill(const moe_dims* d, int Tc, void* ws, size_t* bytes) {
@@ -80,7 +81,8 @@ PrefillWs carve_prefill(const moe_dims* d, int Tc, void* ws, size_t* bytes) {
   w.items = c.take<int32_t>(3 * (size_t)max_items(d, Tc));
   w.num_items = c.take<int32_t>(1);
   w.h = c.take<uint16_t>((size_t)(k + 1) * Tc * d->I);
-  w.partial = c.take<float>((size_t)(k + 1) * Tc * d->H);
+  w.partial_r = c.take<uint16_t>((size_t)k * Tc * d->H);
+  w.partial_s = c.take<float>((size_t)Tc * d->H);
   *bytes = c.used;
   return w;
 }
@@ -397,13 +399,14 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
     g.paired = 0;
     g.act = W.h;
     g.h_out = nullptr;
-    g.partial = W.partial;
+    g.partial_r = W.partial_r;
+    g.partial_s = W.partial_s;
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;
     if (launch_gemm(kDown, g, s, dn_blocks) != hipSuccess) return MOE_EHIP;
 
     // y = bf16(shared + sum of the k weighted expert outputs)
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;
-    if (launch_combine(W.partial, topk_w, y + (int64_t)t0 * H, Tn, H, k, s) != hipSuccess)
+    if (launch_combine(W.partial_r, W.partial_s, topk_w, y + (int64_t)t0 * H, Tn, H, k, s) != hipSuccess)
       return MOE_EHIP;
   }
   if (rec.mark(s) != hipSuccess) return MOE_EHIP;

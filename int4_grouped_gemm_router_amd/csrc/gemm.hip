@@ -86,9 +86,23 @@ struct GemmLds {
   u32x4 sb[S][kWaves][16];              // [stage][wave][c16]: 4 scales, 4 biases
   UnitInfo unit[kBatch];
   int rowidx[kBatch][kItemRows];        // activation row of each item row
-  int outrow[kBatch][kItemRows];        // down: output row t*(k+1) + slot
+  int outrow[kBatch][kItemRows];        // down: pair p (routed) or token t (shared)
   u32x4 tr[kWaves][64];                 // per-wave epilogue transpose (1 KB)
 };
+
+// Down output of one row and four consecutive columns: a routed row (pair p)
+// rounded to bf16 at [p][N] (it enters the combine with a routing weight of
+// about 1/k), a shared-expert row (token t) kept in fp32 at [t][N].
+__device__ inline void store_down(const GemmArgs& a, bool routed, int orow, int col, f32x4 v) {
+  if (routed) {
+    u32x2 o;
+    o.x = f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+    o.y = f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+    *reinterpret_cast<u32x2*>(a.partial_r + (int64_t)orow * a.N + col) = o;
+  } else {
+    *reinterpret_cast<f32x4*>(a.partial_s + (int64_t)orow * a.N + col) = v;
+  }
+}
 
 // bf16 pairs (1.0, 1.0): the B operand that turns an MFMA into row sums.
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
@@ -210,9 +224,9 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs a) {
         int orow;
         if (u.expert >= 0) {
           const int p = a.perm[u.row0 + mm];
-          orow = p + p / a.k;  // row t*(k+1) + j of pair p = t*k + j
+          orow = p;  // routed output row of pair p = t*k + j
         } else {
-          orow = (u.row0 - a.k * a.T + mm) * (a.k + 1) + a.k;
+          orow = u.row0 - a.k * a.T + mm;  // shared output row: the token
         }
         L.outrow[j][m] = orow;
       }
@@ -252,6 +266,7 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs a) {
     f32x4 acc[2][4];
     int cu = 0, cg = 0, st = 0;
     int rows = 0, nsub = 0, nt = 0, row0 = 0;
+    bool routed = true;
     bool active = false;
     for (int s = 0; s < total; ++s) {
       wait_vm(kCopiesPerStep * min(S - 2, total - 1 - s));
@@ -261,6 +276,7 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs a) {
       if (s + S - 1 < total) issue(st == 0 ? S - 1 : st - 1);
       if (cg == 0) {
         rows = __builtin_amdgcn_readfirstlane(L.unit[cu].rows);
+        routed = __builtin_amdgcn_readfirstlane(L.unit[cu].expert) >= 0;
         row0 = __builtin_amdgcn_readfirstlane(L.unit[cu].row0);
         nt = __builtin_amdgcn_readfirstlane(L.unit[cu].nt);
         nsub = (rows + 15) >> 4;
@@ -322,9 +338,7 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs a) {
                   compiler_fence();
                   const f32x4 v = *reinterpret_cast<const f32x4*>(&trf[rr * 16 + 4 * c4]);
                   compiler_fence();
-                  if (r < rows)
-                    *reinterpret_cast<f32x4*>(a.partial + (int64_t)orow * a.N + 64 * wt + 16 * ct +
-                                              4 * c4) = v;
+                  if (r < rows) store_down(a, routed, orow, 64 * wt + 16 * ct + 4 * c4, v);
                 }
               }
             }
@@ -432,9 +446,9 @@ __global__ __launch_bounds__(kRThreads, kRBlocksPerCU) void gemm_ring_kernel(Gem
         int orow;
         if (u.expert >= 0) {
           const int p = a.perm[u.row0 + mm];
-          orow = p + p / a.k;
+          orow = p;
         } else {
-          orow = (u.row0 - a.k * a.T + mm) * (a.k + 1) + a.k;
+          orow = u.row0 - a.k * a.T + mm;  // shared output row: the token
         }
         L.outrow[j][m] = orow;
       }
@@ -485,11 +499,13 @@ __global__ __launch_bounds__(kRThreads, kRBlocksPerCU) void gemm_ring_kernel(Gem
 
     f32x4 acc[2][4];
     int rows = 0, nsub = 0, nt = 0, row0 = 0;
+    bool routed = true;
     bool active = false;
     for (int s0 = 0; s0 < total; s0 += RS) {
       const int cu = s0 / G, cg0 = s0 % G;
       if (cg0 == 0) {
         rows = __builtin_amdgcn_readfirstlane(L.unit[cu].rows);
+        routed = __builtin_amdgcn_readfirstlane(L.unit[cu].expert) >= 0;
         row0 = __builtin_amdgcn_readfirstlane(L.unit[cu].row0);
         nt = __builtin_amdgcn_readfirstlane(L.unit[cu].nt);
         nsub = (rows + 15) >> 4;
@@ -563,8 +579,7 @@ __global__ __launch_bounds__(kRThreads, kRBlocksPerCU) void gemm_ring_kernel(Gem
               compiler_fence();
               const f32x4 v = *reinterpret_cast<const f32x4*>(&trf[rr * 16 + 4 * c4]);
               compiler_fence();
-              if (r < rows)
-                *reinterpret_cast<f32x4*>(a.partial + (int64_t)orow * a.N + 64 * wt + 16 * ct + 4 * c4) = v;
+              if (r < rows) store_down(a, routed, orow, 64 * wt + 16 * ct + 4 * c4, v);
             }
           }
         }
@@ -573,11 +588,13 @@ __global__ __launch_bounds__(kRThreads, kRBlocksPerCU) void gemm_ring_kernel(Gem
   }
 }
 
-// y[t][n] = bf16(partial[t][k][n] + sum_{j<k} w[t][j] * partial[t][j][n]):
-// slot k holds the shared expert, slots j < k the routed experts; each thread
-// owns eight consecutive n of one token and issues all its loads up front.
+// y[t][n] = bf16(shared[t][n] + sum_{j<k} w[t][j] * routed[t k + j][n]), j
+// ascending: the shared expert's fp32 row plus the k routed bf16 rows; each
+// thread owns eight consecutive n of one token and issues all its loads up
+// front.
 template <int K>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partial,
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ routed,
+                                                      const float* __restrict__ shared,
                                                       const float* __restrict__ topk_w,
                                                       uint16_t* __restrict__ y, int T, int N) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -585,21 +602,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (i >= (int64_t)T * per_row) return;
   const int64_t t = i / per_row;
   const int n = (int)(i % per_row) * 8;
-  const float* p = partial + t * (K + 1) * (int64_t)N + n;
-  f32x4 v[K + 1][2];
+  const uint16_t* pr = routed + t * K * (int64_t)N + n;
+  u32x4 v[K];
 #pragma unroll
-  for (int j = 0; j <= K; ++j) {
-    v[j][0] = *reinterpret_cast<const f32x4*>(p + (int64_t)j * N);
-    v[j][1] = *reinterpret_cast<const f32x4*>(p + (int64_t)j * N + 4);
-  }
+  for (int j = 0; j < K; ++j) v[j] = *reinterpret_cast<const u32x4*>(pr + (int64_t)j * N);
+  f32x4 s0 = *reinterpret_cast<const f32x4*>(shared + t * N + n);
+  f32x4 s1 = *reinterpret_cast<const f32x4*>(shared + t * N + n + 4);
   float w[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) w[j] = topk_w[t * K + j];
-  f32x4 s0 = v[K][0], s1 = v[K][1];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    s0 += w[j] * v[j][0];
-    s1 += w[j] * v[j][1];
+    const f32x4 d0 = {bf16lo(v[j].x), bf16hi(v[j].x), bf16lo(v[j].y), bf16hi(v[j].y)};
+    const f32x4 d1 = {bf16lo(v[j].z), bf16hi(v[j].z), bf16lo(v[j].w), bf16hi(v[j].w)};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s0[q] = __builtin_fmaf(w[j], d0[q], s0[q]);
+      s1[q] = __builtin_fmaf(w[j], d1[q], s1[q]);
+    }
   }
   u32x4 o;
   o.x = f2bf(s0.x) | ((uint32_t)f2bf(s0.y) << 16);
@@ -737,12 +757,12 @@ hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t s, int grid
   return mode == kGateUp ? launch_mode<kGateUp>(a, s, grid_blocks) : launch_mode<kDown>(a, s, grid_blocks);
 }
 
-hipError_t launch_combine(const float* partial, const float* topk_w, uint16_t* y, int T, int N,
-                          int k, hipStream_t s) {
+hipError_t launch_combine(const uint16_t* routed, const float* shared, const float* topk_w, uint16_t* y,
+                          int T, int N, int k, hipStream_t s) {
   if (k != 8) return hipErrorInvalidValue;
   const int64_t threads = (int64_t)T * (N / 8);
   hipLaunchKernelGGL(combine_kernel<8>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                     partial, topk_w, y, T, N);
+                     routed, shared, topk_w, y, T, N);
   return hipGetLastError();
 }
 

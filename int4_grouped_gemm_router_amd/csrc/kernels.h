@@ -57,7 +57,8 @@ struct GemmArgs {
   const int32_t* perm;       // [kT]
   // outputs
   uint16_t* h_out;           // gate/up: h [(k+1)T][N] bf16
-  float* partial;            // down: [T][k+1][N] fp32; slot j < k routed, slot k shared
+  uint16_t* partial_r;       // down, routed rows: [T*k][N] bf16 at pair p = t*k + j
+  float* partial_s;          // down, shared-expert rows: [T][N] fp32
 };
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* planes, float* partial, int T, int H,
@@ -68,9 +69,9 @@ hipError_t launch_fill_zero(int* p, int n, hipStream_t s);
 // grid_blocks > 0: that many blocks (rounded up to a multiple of 8) instead
 // of the persistent grid (used when the host knows the exact unit count).
 hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t s, int grid_blocks = 0);
-// y[t][n] = bf16(partial[t][k][n] + sum_{j<k} topk_w[t][j] * partial[t][j][n]) (fixed order).
-hipError_t launch_combine(const float* partial, const float* topk_w, uint16_t* y, int T, int N,
-                          int k, hipStream_t s);
+// y[t][n] = bf16(shared[t][n] + sum_{j<k} topk_w[t][j] * routed[t*k + j][n]) (j ascending).
+hipError_t launch_combine(const uint16_t* routed, const float* shared, const float* topk_w, uint16_t* y,
+                          int T, int N, int k, hipStream_t s);
 // The unfused comparison path: every expert of a packed blob with rows (hist
 // null or hist[e] > 0), and the shared expert, expanded to bf16 w = q s + b
 // (one rounding) into `out` / `out_shared` in the kBf16GroupBytes layout.
