@@ -24,23 +24,30 @@ namespace moe {
 
 // ---------------------------------------------------------------- router
 
-// Grid: (ceil(T/64), E/64, KS). Block: 256 threads = 4 waves; wave w owns
-// tokens [64*bx + 16w, +16) and all 64 experts of the tile (4 MFMA tiles).
+// Grid: (ceil(T/(16 NW)), E/64, KS). Block: NW waves (4, or 8 for long
+// chunks, which halves how often the weight tile is re-read); wave w owns
+// tokens [16 NW bx + 16w, +16) and all 64 experts of the tile (4 MFMA tiles).
 // The three bf16 planes of the 64-expert weight tile (24 KB per 64-input
-// group) are shared by the four waves: they arrive in a three-stage LDS ring
-// by asynchronous global -> LDS copies, six 1 KB copies per wave per group;
+// group) are shared by the waves: they arrive in a three-stage LDS ring by
+// asynchronous global -> LDS copies, 24 / NW 1 KB copies per wave per group;
 // the activation fragments arrive in a register ring alongside.
 constexpr int kRStages = 3;
 
+template <int NW>
 __device__ inline void router_wait(int groups) {
-  // eight loads per group per wave: six plane copies and two activation loads
-  if (groups >= 1)
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else
+  // 24 / NW + 2 loads per group per wave: the plane copies and two activation loads
+  if (groups >= 1) {
+    if constexpr (NW == 8)
+      asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
 }
 
-__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ planes,
                                                           float* __restrict__ partial, int T,
                                                           int H, int E, int groups_per_split,
@@ -55,7 +62,9 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
   if (zero_buf && tt == 0 && et == 0 && split == 0)
     for (int i = threadIdx.x; i < zero_count; i += blockDim.x) zero_buf[i] = 0;
 
-  const int row = tt * 64 + wave * 16 + c16;
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  constexpr int kCopies = 24 / NW;  // 1 KB plane copies per wave and group
+  const int row = tt * 16 * NW + wave * 16 + c16;
   const bool row_ok = row < T;
   const uint16_t* xr = x + (int64_t)(row_ok ? row : 0) * H + 8 * kb;
   const uint8_t* pl = reinterpret_cast<const uint8_t*>(planes);
@@ -64,8 +73,8 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
   auto issue = [&](int gi, int st) {
     const int g = g0 + gi;
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int q = wave * 6 + i;            // 1 KB chunk of the 24 KB tile
+    for (int i = 0; i < kCopies; ++i) {
+      const int q = wave * kCopies + i;      // 1 KB chunk of the 24 KB tile
       const int p = q >> 3, part = q & 7;
       const uint8_t* src = pl + ((((int64_t)p * n_et + et) * G + g) * 8 + part) * 1024 + lane * 16;
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&bt[st][p * 512 + part * 64], 16, 0, 0);
@@ -83,7 +92,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
     for (int d = 0; d < kRStages; ++d) {
       const int gi = gb + d;
       if (gi >= ng) break;
-      router_wait(min(kRStages - 2, ng - 1 - gi));
+      router_wait<NW>(min(kRStages - 2, ng - 1 - gi));
       lds_barrier();
       if (gi + kRStages - 1 < ng) issue(gi + kRStages - 1, (d + kRStages - 1) % kRStages);
       const u32x4 a0 = row_ok ? aq[d][0] : u32x4{0u, 0u, 0u, 0u};
@@ -100,7 +109,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
   float* out = partial + (int64_t)split * T * E;
   for (int ct = 0; ct < 4; ++ct)
     for (int i = 0; i < 4; ++i) {
-      const int t = tt * 64 + wave * 16 + 4 * kb + i;
+      const int t = tt * 16 * NW + wave * 16 + 4 * kb + i;
       if (t < T) out[(int64_t)t * E + et * 64 + ct * 16 + c16] = acc[ct][i];
     }
 }
@@ -288,12 +297,22 @@ __global__ void fill_zero_kernel(int* p, int n) {
 
 // ---------------------------------------------------------------- launchers
 
+// From this many tokens the router takes 128-token tiles (8 waves per block;
+// below it, 64-token tiles keep enough blocks to fill the chip).
+constexpr int kRouterWideMinT = 1024;
+
 hipError_t launch_router(const uint16_t* x, const uint16_t* planes, float* partial, int T, int H,
                          int E, int splits, int* zero_buf, int zero_count, hipStream_t s) {
   const int G = H / kGroup;
-  dim3 grid((T + 63) / 64, E / 64, splits);
-  hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(256), 0, s, x, planes, partial, T, H, E,
-                     G / splits, zero_buf, zero_count);
+  if (T >= kRouterWideMinT) {
+    const dim3 grid((T + 127) / 128, E / 64, splits);
+    hipLaunchKernelGGL(router_mfma_kernel<8>, grid, dim3(512), 0, s, x, planes, partial, T, H, E,
+                       G / splits, zero_buf, zero_count);
+  } else {
+    const dim3 grid((T + 63) / 64, E / 64, splits);
+    hipLaunchKernelGGL(router_mfma_kernel<4>, grid, dim3(256), 0, s, x, planes, partial, T, H, E,
+                       G / splits, zero_buf, zero_count);
+  }
   return hipGetLastError();
 }
 

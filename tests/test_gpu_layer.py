@@ -165,6 +165,11 @@ def test_prefill_skew_t2048_sampled(torch_cuda):
                                        heavy_tokens[:: max(1, len(heavy_tokens) // 64)][:64]]))
     s = check_layer(x, w, y, logits, idx, wsel, tokens=sample)
     print(f"skew T=2048 ({len(sample)} sampled): {s}")
+    # the same prompt in 512-token chunks (64-token router tiles instead of
+    # 128-token ones): identical logits and outputs
+    y2, logits2, _ = _prefill(torch_cuda, dw, x, chunk=512, route=False)
+    assert np.array_equal(logits, logits2)
+    assert np.array_equal(y, y2)
 
 
 def test_prefill_long_chunked_sampled(torch_cuda):
