@@ -270,9 +270,11 @@ def test_decode_tiny_and_vs_prefill(torch_cuda):
 # shapes do not: (1024, 384, E=128): gate/up over 16 groups, down over K = 384
 # (6 groups, the LDS-stream GEMM); (4096, 256, E=64): gate/up over 64 groups
 # (the most the GEMMs and the decode kernels take), down over 4 groups;
-# (768, 640, E=192): 12 and 10 groups. Prefill on a ragged 40-token batch,
+# (768, 640, E=192): 12 and 10 groups; (256, 4096, E=64): the largest
+# intermediate size, down over 64 groups (eight rounds in the decode down
+# kernel) and 128 gate/up wave tiles. Prefill on a ragged 40-token batch,
 # then decode at T = 1 and 4.
-@pytest.mark.parametrize("H,I,E", [(1024, 384, 128), (4096, 256, 64), (768, 640, 192)])
+@pytest.mark.parametrize("H,I,E", [(1024, 384, 128), (4096, 256, 64), (768, 640, 192), (256, 4096, 64)])
 def test_other_family_sizes(torch_cuda, H, I, E):
     rng = np.random.default_rng(H + I + E)
     w = synth.make_weights(rng, H, I, E)
