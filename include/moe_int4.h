@@ -58,7 +58,12 @@ typedef struct {
   int32_t H, I, E, top_k, block_m;
 } moe_dims;
 
-/* Device weights of one layer. Every pointer is a device pointer. */
+/* Device weights of one layer. Every pointer is a device pointer. The blobs
+ * must have been packed for the dims passed with them (E, H, I): their
+ * headers are not read at call time, since that would need a device read
+ * and a host synchronisation, so blobs of another shape give wrong results,
+ * not an error code. The caller keeps them alive until the stream work that
+ * uses them completes. */
 typedef struct {
   const void* router_w3;       /* pack_router_bf16x3 blob of Wr (prefill router)     */
   const float* router_w;       /* [E][H] fp32 Wr, row-major (decode router)           */
