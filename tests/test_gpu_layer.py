@@ -256,6 +256,29 @@ def test_decode_matches_oracle(torch_cuda, T):
         print(f"decode T={T} step {step}: {s}")
 
 
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_skewed_router_bias(torch_cuda, T):
+    # the skewed layer's per-expert logit bias goes through the decode router
+    # kernel; with it most tokens pick from a few heavy experts, so at T = 4
+    # the tokens share experts (fewer unique experts than pairs)
+    wl, w, dw = _layer("skew_t2048")
+    assert w.router_bias is not None
+    rng = np.random.default_rng(70 + T)
+    uniq_counts = []
+    for step in range(3):
+        x = synth.make_x(rng, T, w.H)
+        y, logits, meta = _decode(torch_cuda, dw, x)
+        idx, wsel = _route_of(meta, T)
+        s = check_layer(x, w, y, logits, idx, wsel)
+        check_route_meta(meta, idx, 256, 8, 32)
+        uniq = np.unique(idx)
+        assert meta["num_blocks"] == len(uniq)
+        uniq_counts.append(len(uniq))
+        print(f"skewed decode T={T} step {step}: {s}")
+    if T == 4:
+        assert min(uniq_counts) < 8 * T, "skewed routing should make tokens share experts"
+
+
 def test_decode_tiny_and_vs_prefill(torch_cuda):
     _, w, dw = _layer("tiny_t32")
     x = synth.make_x(np.random.default_rng(11), 4, w.H)
