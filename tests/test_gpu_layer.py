@@ -197,6 +197,26 @@ def test_prefill_long_chunked_sampled(torch_cuda):
     print(f"long T=16384 chunk 4096 ({len(sample)} sampled): {s}")
 
 
+def test_prefill_ragged_chunks(torch_cuda):
+    # 100 tokens in chunks of 32 (32, 32, 32, 4): every token against the
+    # oracle, bit-identical to the unchunked call, and the route output holds
+    # the last (4-token) chunk's metadata
+    _, w, dw = _layer("tiny_t32")
+    x = synth.make_x(np.random.default_rng(21), 100, w.H)
+    y, logits, meta = _prefill(torch_cuda, dw, x, chunk=32)
+    y1, logits1, _ = _prefill(torch_cuda, dw, x, chunk=0, route=False)
+    assert np.array_equal(y, y1) and np.array_equal(logits, logits1)
+    idx_last, _ = _route_of(meta, 4)
+    check_route_meta(meta, idx_last, 256, 8, 32)
+    d = dw.dims
+    ro = B.RouteBuffers(d, 100)
+    B.moe_route(d, torch_cuda.from_numpy(logits).cuda(), 100, ro, B.workspace(d, 100, B.MODE_ROUTE))
+    torch_cuda.cuda.synchronize()
+    idx_all, w_all = _route_of(ro.to_numpy(), 100)
+    assert np.array_equal(idx_all[-4:], idx_last)
+    check_layer(x, w, y, logits, idx_all, w_all)
+
+
 def test_prefill_forced_heavy_routing(torch_cuda):
     # a router bias that sends nearly every token to experts 0..7 and 100..103:
     # groups of hundreds of rows, 244 empty experts, ragged 64-row items
@@ -240,7 +260,7 @@ def _decode(torch, dw, x):
     return y.cpu().numpy().view(np.uint16), logits.cpu().numpy(), ro.to_numpy()
 
 
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
 def test_decode_matches_oracle(torch_cuda, T):
     wl, w, dw = _layer("prefill_t512")
     rng = np.random.default_rng(40 + T)
