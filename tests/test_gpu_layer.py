@@ -217,6 +217,24 @@ def test_prefill_ragged_chunks(torch_cuda):
     check_layer(x, w, y, logits, idx_all, w_all)
 
 
+def test_zero_input_exact(torch_cuda):
+    # x = 0: every logit is 0, so the selection is experts 0..7 (ties to the
+    # lower index) with weights exactly 1/8, every product is 0 and y is +0
+    # bit for bit, through prefill and decode alike
+    _, w, dw = _layer("tiny_t32")
+    for T in (1, 4, 37):
+        x = np.zeros((T, w.H), np.uint16)
+        outs = [_prefill(torch_cuda, dw, x)]
+        if T <= 4:
+            outs.append(_decode(torch_cuda, dw, x))
+        for y, logits, meta in outs:
+            assert not y.any(), "y must be +0 everywhere"
+            assert not logits.any()
+            idx, wsel = _route_of(meta, T)
+            assert np.array_equal(idx, np.tile(np.arange(8), (T, 1)))
+            assert np.all(wsel == np.float32(0.125))
+
+
 def test_prefill_forced_heavy_routing(torch_cuda):
     # a router bias that sends nearly every token to experts 0..7 and 100..103:
     # groups of hundreds of rows, 244 empty experts, ragged 64-row items
