@@ -27,6 +27,11 @@
  *    surface at the caller's next synchronisation.
  *  - Return value: MOE_OK (0) or a negative MOE_E* code. Arguments are checked
  *    before anything is enqueued, so on error nothing has been launched.
+ *  - Alignment: x, y, the workspace, the unfused weight buffer, router_w and
+ *    the packed blobs must be 16-byte aligned (the kernels move them in
+ *    16-byte vectors); logits, logits_out, router_bias and the route_out
+ *    arrays 4-byte aligned. Misaligned pointers give MOE_EINVAL. (Fresh
+ *    torch / hipMalloc allocations are 256-byte aligned.)
  *  - Supported dims: E <= 256 and E % 64 == 0, top_k == 8, block_m 32 or 16
  *    (the routing block size, which is also the row count of the grouped
  *    GEMMs' work items; diariobitcoin.com, "Perplexity libera Lily...",
@@ -45,7 +50,7 @@ extern "C" {
 #endif
 
 #define MOE_OK 0
-#define MOE_EINVAL (-1)       /* null pointer, negative size, bad enum        */
+#define MOE_EINVAL (-1)       /* null or misaligned pointer, negative size, bad enum */
 #define MOE_EUNSUPPORTED (-2) /* dims outside the supported set above         */
 #define MOE_EWORKSPACE (-3)   /* workspace smaller than moe_workspace_bytes   */
 #define MOE_EHIP (-4)         /* a HIP launch reported an error               */

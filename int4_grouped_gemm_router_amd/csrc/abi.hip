@@ -1,6 +1,7 @@
 // C ABI of the int4 MoE library: argument checks, workspace carve-up, the
 // chunk loop, and the launches on the caller's stream (include/moe_int4.h).
 #include <algorithm>
+#include <cstdint>
 
 #include "../../include/moe_int4.h"
 #include "kernels.h"
@@ -111,9 +112,23 @@ size_t route_ws(const moe_dims* d, int T, void* ws, int32_t** chunk_hist) {
   return c.used;
 }
 
+// The kernels move activations, outputs, workspace pieces and packed weights
+// in 16-byte vectors and everything else in 4-byte words; a misaligned
+// pointer is rejected before anything is enqueued (null passes: null checks
+// are separate).
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
 bool route_out_ok(const moe_route_out* o) {
   return o && o->topk_idx && o->topk_w && o->hist && o->offsets && o->perm && o->inv_perm &&
-         o->block_map && o->num_blocks;
+         o->block_map && o->num_blocks && al4(o->topk_idx) && al4(o->topk_w) && al4(o->hist) &&
+         al4(o->offsets) && al4(o->perm) && al4(o->inv_perm) && al4(o->block_map) &&
+         al4(o->num_blocks);
+}
+
+bool weights_aligned(const moe_layer_weights* w) {
+  return al16(w->router_w3) && al16(w->router_w) && al4(w->router_bias) && al16(w->experts_gate_up) &&
+         al16(w->experts_down) && al16(w->shared_gate_up) && al16(w->shared_down);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
@@ -174,7 +189,7 @@ int moe_route(const moe_dims* dims, const float* logits, int32_t T, const moe_ro
   if (!dims || T < 0) return MOE_EINVAL;
   if (!dims_ok(dims)) return MOE_EUNSUPPORTED;
   if (T == 0) return MOE_OK;
-  if (!logits || !route_out_ok(out) || !ws) return MOE_EINVAL;
+  if (!logits || !route_out_ok(out) || !ws || !al4(logits) || !al16(ws)) return MOE_EINVAL;
   int32_t* chunk_hist;
   if (ws_bytes < route_ws(dims, T, nullptr, &chunk_hist)) return MOE_EWORKSPACE;
   route_ws(dims, T, ws, &chunk_hist);
@@ -235,7 +250,7 @@ int moe_prefill_layer_unfused(const moe_dims* dims, const moe_layer_weights* w, 
   size_t need = 0;
   const int rc = moe_unfused_weight_bytes(dims, &need);
   if (rc != MOE_OK) return rc;
-  if (!wbuf) return MOE_EINVAL;
+  if (!wbuf || !al16(wbuf)) return MOE_EINVAL;
   if (wbuf_bytes < need) return MOE_EBUFFER;
   return prefill_impl(dims, w, x, y, T, chunk_T, nullptr, nullptr, ws, ws_bytes, stream,
                       Recorder{}, false, static_cast<uint8_t*>(wbuf));
@@ -273,6 +288,7 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
       !w->shared_gate_up || !w->shared_down)
     return MOE_EINVAL;
   if (route_out && !route_out_ok(route_out)) return MOE_EINVAL;
+  if (!al16(x) || !al16(y) || !al16(ws) || !al4(logits_out) || !weights_aligned(w)) return MOE_EINVAL;
   const int Tc = (chunk_T <= 0 || chunk_T > T) ? T : chunk_T;
   size_t need;
   carve_prefill(dims, Tc, nullptr, &need);
@@ -446,6 +462,7 @@ int decode_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_t
       !w->shared_gate_up || !w->shared_down)
     return MOE_EINVAL;
   if (route_out && !route_out_ok(route_out)) return MOE_EINVAL;
+  if (!al16(x) || !al16(y) || !al16(ws) || !al4(logits_out) || !weights_aligned(w)) return MOE_EINVAL;
   size_t need;
   carve_decode(dims, T, nullptr, &need);
   if (ws_bytes < need) return MOE_EWORKSPACE;
@@ -503,7 +520,7 @@ const char* moe_strerror(int code) {
 
 int moe_test_dequant(const void* blob, int32_t count, int32_t N, int32_t K, int32_t paired,
                      int32_t expert, float* out, void* stream) {
-  if (!blob || !out || expert < 0 || expert >= count) return MOE_EINVAL;
+  if (!blob || !out || expert < 0 || expert >= count || !al16(blob) || !al4(out)) return MOE_EINVAL;
   if (moe_packed_bytes(count, N, K, paired) == 0) return MOE_EUNSUPPORTED;
   const PackGeom g = pack_geom(N, K, paired);
   const uint8_t* base = static_cast<const uint8_t*>(blob) + kHeaderBytes + (int64_t)expert * g.expert_bytes;

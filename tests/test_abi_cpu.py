@@ -160,6 +160,43 @@ def test_entry_points_reject_bad_arguments():
     assert B.strerror(B.MOE_EWORKSPACE) == "workspace too small"
 
 
+def test_entry_points_reject_misaligned_pointers():
+    # 16-byte vectors for activations, outputs, workspace and packed weights,
+    # 4-byte words for logits and routing metadata: misaligned pointers are
+    # rejected before any launch
+    L = B.lib()
+    d = B.dims(2048, 512)
+    by = ctypes.byref
+    w = B.MoeLayerWeights(*([FAKE] * 7))
+    ws = B.moe_workspace_bytes(d, 64, B.MODE_PREFILL)
+    dws = B.moe_workspace_bytes(d, 1, B.MODE_DECODE)
+    ro = _route_out(d)
+
+    def prefill(x=FAKE, y=FAKE, logits=None, wts=w, wsp=FAKE):
+        return L.moe_prefill_layer(by(d), by(wts), x, y, 64, 0, logits, None, wsp, ws, None)
+
+    for kw in ({"x": FAKE + 2}, {"y": FAKE + 8}, {"wsp": FAKE + 4}, {"logits": FAKE + 2}):
+        assert prefill(**kw) == B.MOE_EINVAL, kw
+    for i in (0, 3, 4, 5, 6):  # router_w3 and the four blobs
+        fields = [FAKE] * 7
+        fields[i] = FAKE + 8
+        assert prefill(wts=B.MoeLayerWeights(*fields)) == B.MOE_EINVAL, i
+    fields = [FAKE] * 7
+    fields[2] = FAKE + 2  # router_bias
+    assert prefill(wts=B.MoeLayerWeights(*fields)) == B.MOE_EINVAL
+    assert L.moe_decode_layer(by(d), by(w), FAKE + 4, FAKE, 1, None, None, FAKE, dws,
+                              None) == B.MOE_EINVAL
+    fields = [FAKE] * 7
+    fields[1] = FAKE + 4  # router_w (decode)
+    assert L.moe_decode_layer(by(d), by(B.MoeLayerWeights(*fields)), FAKE, FAKE, 1, None, None,
+                              FAKE, dws, None) == B.MOE_EINVAL
+    rws = B.moe_workspace_bytes(d, 4, B.MODE_ROUTE)
+    assert L.moe_route(by(d), FAKE + 2, 4, by(ro), FAKE, rws, None) == B.MOE_EINVAL
+    bad_ro = B.MoeRouteOut(*([FAKE] * 7 + [FAKE + 1]))
+    assert L.moe_route(by(d), FAKE, 4, by(bad_ro), FAKE, rws, None) == B.MOE_EINVAL
+    assert L.moe_test_dequant(FAKE + 8, 2, 64, 64, 0, 0, FAKE, None) == B.MOE_EINVAL
+
+
 def test_workspace_and_block_bounds():
     d = B.dims(2048, 512)
     assert B.moe_max_blocks(d, 2048) == 2048 * 8 // 32 + 256
