@@ -37,7 +37,8 @@
  *    GEMMs' work items; diariobitcoin.com, "Perplexity libera Lily...",
  *    section "Las optimizaciones en el prefill": 32-row blocks replaced
  *    16-row ones), H % 256 == 0 (H <= 4096), I % 128 == 0
- *    (I <= 4096).
+ *    (I <= 4096), and T * top_k < 2^30 tokens x slots per call (pair
+ *    indices are 32-bit).
  */
 #ifndef MOE_INT4_H
 #define MOE_INT4_H

@@ -119,6 +119,10 @@ size_t route_ws(const moe_dims* d, int T, void* ws, int32_t** chunk_hist) {
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
 
+// (token, slot) pair indices are 32-bit in the kernels
+constexpr int64_t kMaxPairs = int64_t(1) << 30;
+bool too_many_pairs(const moe_dims* d, int64_t T) { return T * d->top_k >= kMaxPairs; }
+
 bool route_out_ok(const moe_route_out* o) {
   return o && o->topk_idx && o->topk_w && o->hist && o->offsets && o->perm && o->inv_perm &&
          o->block_map && o->num_blocks && al4(o->topk_idx) && al4(o->topk_w) && al4(o->hist) &&
@@ -168,7 +172,7 @@ int64_t moe_max_blocks(const moe_dims* dims, int32_t T) {
 
 int moe_workspace_bytes(const moe_dims* dims, int32_t T_chunk, int32_t mode, size_t* bytes) {
   if (!bytes || T_chunk < 0) return MOE_EINVAL;
-  if (!dims_ok(dims)) return MOE_EUNSUPPORTED;
+  if (!dims_ok(dims) || too_many_pairs(dims, T_chunk)) return MOE_EUNSUPPORTED;
   const int T = std::max(T_chunk, 1);
   if (mode == 0) {
     carve_prefill(dims, T, nullptr, bytes);
@@ -187,7 +191,7 @@ int moe_workspace_bytes(const moe_dims* dims, int32_t T_chunk, int32_t mode, siz
 int moe_route(const moe_dims* dims, const float* logits, int32_t T, const moe_route_out* out,
               void* ws, size_t ws_bytes, void* stream) {
   if (!dims || T < 0) return MOE_EINVAL;
-  if (!dims_ok(dims)) return MOE_EUNSUPPORTED;
+  if (!dims_ok(dims) || too_many_pairs(dims, T)) return MOE_EUNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!logits || !route_out_ok(out) || !ws || !al4(logits) || !al16(ws)) return MOE_EINVAL;
   int32_t* chunk_hist;
@@ -282,7 +286,7 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
                  void* ws, size_t ws_bytes, void* stream, Recorder rec, bool host_routed,
                  uint8_t* unfused_w) {
   if (!dims || T < 0) return MOE_EINVAL;
-  if (!dims_ok(dims)) return MOE_EUNSUPPORTED;
+  if (!dims_ok(dims) || too_many_pairs(dims, T)) return MOE_EUNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!w || !x || !y || !ws || !w->router_w3 || !w->experts_gate_up || !w->experts_down ||
       !w->shared_gate_up || !w->shared_down)

@@ -158,6 +158,13 @@ def test_entry_points_reject_bad_arguments():
         n = ctypes.c_size_t(0)
         assert L.moe_workspace_bytes(by(dd), 64, 0, by(n)) == B.MOE_EUNSUPPORTED
     assert B.strerror(B.MOE_EWORKSPACE) == "workspace too small"
+    # pair indices are 32-bit: T * top_k must stay below 2^30
+    big = 1 << 27
+    assert L.moe_prefill_layer(by(d), by(w), FAKE, FAKE, big, 4096, None, None, FAKE, 1 << 40,
+                               None) == B.MOE_EUNSUPPORTED
+    assert L.moe_route(by(d), FAKE, big, by(ro), FAKE, 1 << 40, None) == B.MOE_EUNSUPPORTED
+    n = ctypes.c_size_t(0)
+    assert L.moe_workspace_bytes(by(d), big, 0, by(n)) == B.MOE_EUNSUPPORTED
 
 
 def test_entry_points_reject_misaligned_pointers():
