@@ -390,6 +390,58 @@ def test_prefill_graph_replay_matches_eager(torch_cuda):
         assert torch.equal(y, y_eager)
 
 
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_graph_replay_matches_eager(torch_cuda, T):
+    """Three decode steps (different tokens) captured in one HIP graph and
+    replayed with eager work and synchronisations in between: outputs,
+    logits and routing metadata equal the eager ones every time."""
+    torch = torch_cuda
+    wl, w, dw = _layer("prefill_t512")
+    d = dw.dims
+    rng = np.random.default_rng(90 + T)
+    xs = [torch.from_numpy(synth.make_x(rng, T, w.H)).cuda() for _ in range(3)]
+    ws = B.workspace(d, T, B.MODE_DECODE)
+    ys = [torch.empty((T, d.H), dtype=torch.int16, device="cuda") for _ in range(3)]
+    lg = [torch.empty((T, d.E), dtype=torch.float32, device="cuda") for _ in range(3)]
+    ro = [B.RouteBuffers(d, T) for _ in range(3)]
+
+    def steps():
+        for i in range(3):
+            B.moe_decode_layer(d, dw, xs[i], ys[i], T, lg[i], ro[i], ws)
+
+    steps()
+    torch.cuda.synchronize()
+    ref = [(y.clone(), l.clone(), r.to_numpy()) for y, l, r in zip(ys, lg, ro)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        steps()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        steps()
+    for rep in range(3):
+        for y, l, r in zip(ys, lg, ro):
+            y.zero_()
+            l.zero_()
+            for f, _ in B.MoeRouteOut._fields_:
+                getattr(r, f).zero_()
+        ws.fill_(0xA5)                      # the workspace holds no state between calls
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert torch.equal(ys[i], ref[i][0]), f"replay {rep} step {i}: y differs"
+            assert torch.equal(lg[i], ref[i][1]), f"replay {rep} step {i}: logits differ"
+            got = ro[i].to_numpy()
+            for f in ("topk_idx", "topk_w", "hist", "offsets", "perm", "inv_perm", "block_map",
+                      "num_blocks"):
+                assert np.array_equal(np.asarray(got[f]), np.asarray(ref[i][2][f])), (rep, i, f)
+        steps()                               # eager work in between
+        torch.cuda.synchronize()
+
+
 @pytest.mark.gpu
 def test_ceiling_helpers_run():
     """The measurement kernels launch through the C ABI, finish, and leave the
