@@ -442,6 +442,41 @@ def test_decode_graph_replay_matches_eager(torch_cuda, T):
         torch.cuda.synchronize()
 
 
+def test_concurrent_streams_match_sequential(torch_cuda):
+    """A prefill and two decodes enqueued on three streams at once, each with
+    its own workspace, give exactly what the same calls give one after
+    another: the library keeps no state shared between calls."""
+    torch = torch_cuda
+    _, w, dw = _layer("prefill_t512")
+    d = dw.dims
+    rng = np.random.default_rng(123)
+    xp = torch.from_numpy(synth.make_x(rng, 300, w.H)).cuda()
+    xd = [torch.from_numpy(synth.make_x(rng, T, w.H)).cuda() for T in (1, 4)]
+    wsp = B.workspace(d, 300, B.MODE_PREFILL)
+    wsd = [B.workspace(d, T, B.MODE_DECODE) for T in (1, 4)]
+
+    def run(streams):
+        yp = torch.empty((300, d.H), dtype=torch.int16, device="cuda")
+        yd = [torch.empty((T, d.H), dtype=torch.int16, device="cuda") for T in (1, 4)]
+        with torch.cuda.stream(streams[0]):
+            B.moe_prefill_layer(d, dw, xp, yp, 300, 0, None, None, wsp)
+        for i, T in enumerate((1, 4)):
+            with torch.cuda.stream(streams[i + 1]):
+                B.moe_decode_layer(d, dw, xd[i], yd[i], T, None, None, wsd[i])
+        torch.cuda.synchronize()
+        return [yp] + yd
+
+    cur = torch.cuda.current_stream()
+    seq = run([cur, cur, cur])
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    for s_ in streams:
+        s_.wait_stream(cur)
+    for rep in range(3):
+        par = run(streams)
+        for a, b in zip(seq, par):
+            assert torch.equal(a, b), f"repeat {rep}: concurrent result differs"
+
+
 @pytest.mark.gpu
 def test_ceiling_helpers_run():
     """The measurement kernels launch through the C ABI, finish, and leave the
