@@ -16,7 +16,8 @@
 //                   for (unique expert or shared expert) x (64-column wave
 //                   tile); a token set that picks one expert twice shares its
 //                   read; block 0 also writes the routing metadata
-//   decode_down     per token and 32-column half tile of the output: the
+//   decode_down     per token and 16-column tile (32 from two tokens on) of
+//                   the output: the
 //                   down projection of the token's (token, slot) pairs, then
 //                   y = bf16(shared + sum over the token's k slots of
 //                   weight * output) in a fixed order
@@ -162,6 +163,31 @@ __device__ inline void gemv_half(const u32x4 w, const u32x4 sbv, int half, const
     p = dot2(b1.w, xs[7], p);
     acc[c] = __builtin_fmaf(bi[c] - 128.0f * sc[c], xsum, __builtin_fmaf(sc[c], p, acc[c]));
   }
+}
+
+// One column tile ct of a lane's 64-column wave tile for one group: the
+// lane's two code words of ct (w) against its 16 inputs; sw / bw are the
+// scale and bias words holding ct's pair (odd: the high half).
+__device__ inline void gemv_quarter(const u32x2 w, uint32_t sw, uint32_t bw, int odd, const u32x4 x0,
+                                    const u32x4 x1, const ExpandConsts xk, float& acc) {
+  const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  constexpr uint32_t kOnes = 0x3F803F80u;
+  float xsum = 0.f;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) xsum = dot2(xs[d], kOnes, xsum);
+  const u32x4 b0 = expand_codes(w.x, xk);
+  const u32x4 b1 = expand_codes(w.y, xk);
+  float p = 0.f;
+  p = dot2(b0.x, xs[0], p);
+  p = dot2(b0.y, xs[1], p);
+  p = dot2(b0.z, xs[2], p);
+  p = dot2(b0.w, xs[3], p);
+  p = dot2(b1.x, xs[4], p);
+  p = dot2(b1.y, xs[5], p);
+  p = dot2(b1.z, xs[6], p);
+  p = dot2(b1.w, xs[7], p);
+  const float sc = odd ? bf16hi(sw) : bf16lo(sw), bi = odd ? bf16hi(bw) : bf16lo(bw);
+  acc = __builtin_fmaf(bi - 128.0f * sc, xsum, __builtin_fmaf(sc, p, acc));
 }
 
 }  // namespace
@@ -366,26 +392,34 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
   }
 }
 
-// Down projection and combine. Grid: T tokens x H/64 column tiles x 2 halves
-// of 32 columns; block: 8 waves. A block owns the k + 1 (token, slot) pairs
-// of its token, slot k being the shared expert. Per round of eight groups,
-// wave w takes group w of the round: all the pairs' weight loads and, at the
-// same time, the block's copy of the pairs' activation rows into LDS, one
-// barrier, and the arithmetic; the column sums of each pair stay in
-// registers over the rounds. The expert ids and routing weights are read
-// once, up front. Then per pair d[j] = sum over the eight waves in order, and
-// y[t] = bf16(d[k] + sum_{j<k} w[t][j] * d[j]), j ascending.
+// Down projection and combine. Grid: T tokens x H/64 wave tiles x 4 / CT
+// blocks of CT column tiles (16 columns each): CT = 1 at one token (128
+// blocks, each moving half the bytes of a 32-column block), CT = 2 from two
+// tokens on (enough blocks already). Block: 8 waves. A block owns the k + 1
+// (token, slot) pairs of its token, slot k being the shared expert. Per
+// round of eight groups, wave w takes group w of the round: all the pairs'
+// weight loads and, at the same time, the block's copy of the pairs'
+// activation rows into LDS, one barrier, and the arithmetic; the column sums
+// of each pair stay in registers over the rounds. The expert ids and routing
+// weights are read once, up front. Then per pair d[j] = sum over the eight
+// waves in order, and y[t] = bf16(d[k] + sum_{j<k} w[t][j] * d[j]), j
+// ascending.
 constexpr int kDecPairs = kK + 1;
 
+template <int CT>
 __global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs a) {
-  __shared__ float red[kDecWaves][kDecPairs][kWaveCols / 2];
+  static_assert(CT == 1 || CT == 2, "one or two column tiles per block");
+  constexpr int kSub = 4 / CT;  // blocks per 64-column wave tile
+  __shared__ float red[kDecWaves][kDecPairs][16 * CT];
   __shared__ u32x4 hs[kDecPairs][kDecWaves * kGroup / 8];  // [pair][group in round][8 inputs]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kb = lane >> 4;
   const int T = a.T, H = a.H, I = a.I;
   const PackGeom geom = pack_geom(H, I, 0);
-  const int half = blockIdx.x & 1, wt = (blockIdx.x >> 1) % geom.n_wt;
-  const int t = (blockIdx.x >> 1) / geom.n_wt, G = geom.G;
+  const int sub = blockIdx.x % kSub, wt = (blockIdx.x / kSub) % geom.n_wt;
+  const int t = (blockIdx.x / kSub) / geom.n_wt, G = geom.G;
+  const int ct0 = CT * sub;  // first column tile of the block
+  const int half = ct0 >> 1, odd = ct0 & 1;
   const ExpandConsts xk = expand_consts();
   int ex[kDecPairs];
   float wj[kK];
@@ -395,9 +429,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs a) 
     wj[j] = a.topk_w[t * kK + j];
   }
   ex[kK] = -1;  // the shared expert
-  float acc[kDecPairs][2];
+  float acc[kDecPairs][CT];
 #pragma unroll
-  for (int j = 0; j < kDecPairs; ++j) acc[j][0] = acc[j][1] = 0.f;
+  for (int j = 0; j < kDecPairs; ++j)
+#pragma unroll
+    for (int c = 0; c < CT; ++c) acc[j][c] = 0.f;
   for (int r0 = 0; r0 < G; r0 += kDecWaves) {
     const int ng = min(kDecWaves, G - r0), g = r0 + wave;
     static_assert(kDecWaves * kGroup / 8 == 64, "LDS row of the round: 64 chunks of 8 inputs");
@@ -412,14 +448,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs a) 
       const int row = j < kK ? t * kK + j : kK * T + t;
       hv[q] = *reinterpret_cast<const u32x4*>(a.h + (int64_t)row * I + r0 * kGroup + 8 * c);
     }
+    // per pair: the lane's code words of the block's column tiles (16 bytes
+    // of the half, or 8 of them) and its scale / bias record
     u32x4 wq[kDecPairs], sb[kDecPairs];
     const int gl = min(g, G - 1);  // waves past G load group G - 1 and do not use it
 #pragma unroll
     for (int j = 0; j < kDecPairs; ++j) {
       const int e = __builtin_amdgcn_readfirstlane(ex[j]);
       const uint8_t* eb = e >= 0 ? a.dn_blob + (int64_t)e * a.dn_expert_bytes : a.dn_shared;
-      wq[j] = *reinterpret_cast<const u32x4*>(eb + geom.nib_off +
-                                              (((int64_t)wt * G + gl) * 128 + 64 * half + lane) * 16);
+      const uint8_t* np = eb + geom.nib_off + (((int64_t)wt * G + gl) * 128 + 64 * half + lane) * 16;
+      if constexpr (CT == 2) {
+        wq[j] = *reinterpret_cast<const u32x4*>(np);
+      } else {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(np + 8 * odd);
+        wq[j] = u32x4{v.x, v.y, 0u, 0u};
+      }
       sb[j] = *reinterpret_cast<const u32x4*>(eb + geom.sb_off + (((int64_t)wt * G + gl) * 16 + c16) * 16);
     }
     // keep every load of the round ahead of the LDS copy and the arithmetic
@@ -434,21 +477,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs a) 
     if (g < G) {
       const int c = 8 * wave + kb;
 #pragma unroll
-      for (int j = 0; j < kDecPairs; ++j) gemv_half(wq[j], sb[j], half, hs[j][c], hs[j][c + 4], xk, acc[j]);
+      for (int j = 0; j < kDecPairs; ++j) {
+        if constexpr (CT == 2)  // both column tiles of the half share the row sums
+          gemv_half(wq[j], sb[j], half, hs[j][c], hs[j][c + 4], xk, acc[j]);
+        else
+          gemv_quarter(u32x2{wq[j][0], wq[j][1]}, half ? sb[j].y : sb[j].x, half ? sb[j].w : sb[j].z, odd,
+                       hs[j][c], hs[j][c + 4], xk, acc[j][0]);
+      }
     }
   }
 #pragma unroll
   for (int j = 0; j < kDecPairs; ++j) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float v = acc[j][c];
+    for (int cc = 0; cc < CT; ++cc) {
+      float v = acc[j][cc];
       v += __shfl_xor(v, 16);
       v += __shfl_xor(v, 32);
-      if (kb == 0) red[wave][j][16 * c + c16] = v;
+      if (kb == 0) red[wave][j][16 * cc + c16] = v;
     }
   }
   __syncthreads();
-  if (tid < kWaveCols / 2) {
+  if (tid < 16 * CT) {
     const int n = tid;
     float d[kK + 1];
 #pragma unroll
@@ -461,7 +510,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs a) 
     float s = d[kK];
 #pragma unroll
     for (int j = 0; j < kK; ++j) s = __builtin_fmaf(wj[j], d[j], s);
-    a.y[(int64_t)t * H + 64 * wt + 32 * half + n] = f2bf(s);
+    a.y[(int64_t)t * H + 64 * wt + 16 * ct0 + n] = f2bf(s);
   }
 }
 
@@ -503,7 +552,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return e;
   if ((e = launch_gateup(gu.G, slots, gu.n_wt, a.T, s, a)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_down_kernel, dim3(a.T * dn.n_wt * 2), dim3(kDecThreads), 0, s, a);
+  if (a.T == 1)
+    hipLaunchKernelGGL(decode_down_kernel<1>, dim3(a.T * dn.n_wt * 4), dim3(kDecThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_down_kernel<2>, dim3(a.T * dn.n_wt * 2), dim3(kDecThreads), 0, s, a);
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return e;
   return hipGetLastError();
 }
