@@ -7,7 +7,8 @@ seeded inputs already resident in HBM. One step = one call of
 moe_prefill_layer: router, top-k, routing metadata, grouped gate/up + SwiGLU,
 grouped down, shared expert and combine. Four copies of the packed weights
 (about 1.8 GB) are used in rotation so the weights stream from HBM rather
-than from the 256 MB Infinity Cache. The timed loop replays, step by step, a
+than from the 256 MB Infinity Cache (the decode workloads rotate 32 copies,
+so that even the shared expert, used every step, comes from HBM). The timed loop replays, step by step, a
 HIP graph of one layer call per weight copy; an eager pass over the same
 number of steps with HIP events around every launch gives the per-kernel
 times.
