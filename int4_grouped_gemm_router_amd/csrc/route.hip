@@ -33,11 +33,12 @@ namespace moe {
 // the activation fragments arrive in a register ring alongside.
 constexpr int kRStages = 3;
 
-template <int NW>
+template <int LOADS>
 __device__ inline void router_wait(int groups) {
-  // 24 / NW + 2 loads per group per wave: the plane copies and two activation loads
+  // LOADS loads per group per wave: the plane copies and two activation loads
+  static_assert(LOADS == 5 || LOADS == 8, "wait counts of the instantiated tilings");
   if (groups >= 1) {
-    if constexpr (NW == 8)
+    if constexpr (LOADS == 5)
       asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
@@ -46,24 +47,29 @@ __device__ inline void router_wait(int groups) {
   }
 }
 
-template <int NW>
+template <int NW, int CT>
 __global__ __launch_bounds__(NW * 64) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ planes,
                                                           float* __restrict__ partial, int T,
                                                           int H, int E, int groups_per_split,
                                                           int* __restrict__ zero_buf,
                                                           int zero_count) {
-  __shared__ u32x4 bt[kRStages][3 * 512];  // [stage][plane][ct 4][ks 2][lane 64]
+  // CT of the four 16-expert column tiles of a 64-expert plane tile per block
+  __shared__ u32x4 bt[kRStages][3 * 2 * CT * 64];  // [stage][plane][ct][ks 2][lane 64]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, kb = lane >> 4;
-  const int tt = blockIdx.x, et = blockIdx.y, split = blockIdx.z;
+  const int tt = blockIdx.x, split = blockIdx.z;
+  const int et = blockIdx.y / (4 / CT), ct0 = CT * (blockIdx.y % (4 / CT));
   const int G = H / kGroup, n_et = E / 64;
-  if (zero_buf && tt == 0 && et == 0 && split == 0)
+  if (zero_buf && tt == 0 && blockIdx.y == 0 && split == 0)
     for (int i = threadIdx.x; i < zero_count; i += blockDim.x) zero_buf[i] = 0;
 
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
-  constexpr int kCopies = 24 / NW;  // 1 KB plane copies per wave and group
+  static_assert(CT == 2 || CT == 4, "half or whole plane tiles");
+  constexpr int kChunks = 3 * 2 * CT;       // 1 KB plane chunks per group
+  constexpr int kCopies = kChunks / NW;     // per wave
+  static_assert(kCopies * NW == kChunks, "chunks split evenly over the waves");
   const int row = tt * 16 * NW + wave * 16 + c16;
   const bool row_ok = row < T;
   const uint16_t* xr = x + (int64_t)(row_ok ? row : 0) * H + 8 * kb;
@@ -74,16 +80,18 @@ __global__ __launch_bounds__(NW * 64) void router_mfma_kernel(const uint16_t* __
     const int g = g0 + gi;
 #pragma unroll
     for (int i = 0; i < kCopies; ++i) {
-      const int q = wave * kCopies + i;      // 1 KB chunk of the 24 KB tile
-      const int p = q >> 3, part = q & 7;
-      const uint8_t* src = pl + ((((int64_t)p * n_et + et) * G + g) * 8 + part) * 1024 + lane * 16;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&bt[st][p * 512 + part * 64], 16, 0, 0);
+      const int q = wave * kCopies + i;      // 1 KB chunk of the block's share
+      const int p = q / (2 * CT), part = q % (2 * CT);
+      const uint8_t* src =
+          pl + ((((int64_t)p * n_et + et) * G + g) * 8 + 2 * ct0 + part) * 1024 + lane * 16;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&bt[st][(p * 2 * CT + part) * 64],
+                                       16, 0, 0);
     }
     aq[st][0] = *reinterpret_cast<const u32x4*>(xr + g * kGroup);
     aq[st][1] = *reinterpret_cast<const u32x4*>(xr + g * kGroup + 32);
   };
-  f32x4 acc[4];
-  for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[CT];
+  for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int d = 0; d < kRStages - 1; ++d)
     if (d < ng) issue(d, d);
@@ -92,7 +100,7 @@ __global__ __launch_bounds__(NW * 64) void router_mfma_kernel(const uint16_t* __
     for (int d = 0; d < kRStages; ++d) {
       const int gi = gb + d;
       if (gi >= ng) break;
-      router_wait<NW>(min(kRStages - 2, ng - 1 - gi));
+      router_wait<kCopies + 2>(min(kRStages - 2, ng - 1 - gi));
       lds_barrier();
       if (gi + kRStages - 1 < ng) issue(gi + kRStages - 1, (d + kRStages - 1) % kRStages);
       const u32x4 a0 = row_ok ? aq[d][0] : u32x4{0u, 0u, 0u, 0u};
@@ -100,17 +108,17 @@ __global__ __launch_bounds__(NW * 64) void router_mfma_kernel(const uint16_t* __
 #pragma unroll
       for (int p = 0; p < 3; ++p)
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          acc[ct] = mfma16(a0, bt[d][p * 512 + (2 * ct) * 64 + lane], acc[ct]);
-          acc[ct] = mfma16(a1, bt[d][p * 512 + (2 * ct + 1) * 64 + lane], acc[ct]);
+        for (int ct = 0; ct < CT; ++ct) {
+          acc[ct] = mfma16(a0, bt[d][(p * 2 * CT + 2 * ct) * 64 + lane], acc[ct]);
+          acc[ct] = mfma16(a1, bt[d][(p * 2 * CT + 2 * ct + 1) * 64 + lane], acc[ct]);
         }
     }
   }
   float* out = partial + (int64_t)split * T * E;
-  for (int ct = 0; ct < 4; ++ct)
+  for (int ct = 0; ct < CT; ++ct)
     for (int i = 0; i < 4; ++i) {
       const int t = tt * 16 * NW + wave * 16 + 4 * kb + i;
-      if (t < T) out[(int64_t)t * E + et * 64 + ct * 16 + c16] = acc[ct][i];
+      if (t < T) out[(int64_t)t * E + et * 64 + (ct0 + ct) * 16 + c16] = acc[ct][i];
     }
 }
 
@@ -306,11 +314,11 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* planes, float* parti
   const int G = H / kGroup;
   if (T >= kRouterWideMinT) {
     const dim3 grid((T + 127) / 128, E / 64, splits);
-    hipLaunchKernelGGL(router_mfma_kernel<8>, grid, dim3(512), 0, s, x, planes, partial, T, H, E,
+    hipLaunchKernelGGL((router_mfma_kernel<8, 4>), grid, dim3(512), 0, s, x, planes, partial, T, H, E,
                        G / splits, zero_buf, zero_count);
   } else {
-    const dim3 grid((T + 63) / 64, E / 64, splits);
-    hipLaunchKernelGGL(router_mfma_kernel<4>, grid, dim3(256), 0, s, x, planes, partial, T, H, E,
+    const dim3 grid((T + 63) / 64, E / 32, splits);
+    hipLaunchKernelGGL((router_mfma_kernel<4, 2>), grid, dim3(256), 0, s, x, planes, partial, T, H, E,
                        G / splits, zero_buf, zero_count);
   }
   return hipGetLastError();
