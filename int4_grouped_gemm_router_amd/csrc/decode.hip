@@ -32,8 +32,6 @@ constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kK = 8;  // experts per token
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
                                          false);

@@ -53,11 +53,17 @@ __device__ inline float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ inline float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 __device__ inline float bf16f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
-// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
-__device__ inline uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Round-to-nearest-even fp32 -> bf16 bits: the conversion instruction of
+// this target (v_cvt_pk_bf16_f32), bit-identical on finite inputs to adding
+// 0x7FFF plus the kept LSB and truncating.
+__device__ inline uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two values rounded to bf16 in one conversion: lo in bits 0..15, hi in 16..31.
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // Split an fp32 value into a truncated bf16 head and the bf16 of the rest.

@@ -96,8 +96,8 @@ struct GemmLds {
 __device__ inline void store_down(const GemmArgs& a, bool routed, int orow, int col, f32x4 v) {
   if (routed) {
     u32x2 o;
-    o.x = f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
-    o.y = f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+    o.x = pack_bf16x2(v.x, v.y);
+    o.y = pack_bf16x2(v.z, v.w);
     *reinterpret_cast<u32x2*>(a.partial_r + (int64_t)orow * a.N + col) = o;
   } else {
     *reinterpret_cast<f32x4*>(a.partial_s + (int64_t)orow * a.N + col) = v;
@@ -622,10 +622,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     }
   }
   u32x4 o;
-  o.x = f2bf(s0.x) | ((uint32_t)f2bf(s0.y) << 16);
-  o.y = f2bf(s0.z) | ((uint32_t)f2bf(s0.w) << 16);
-  o.z = f2bf(s1.x) | ((uint32_t)f2bf(s1.y) << 16);
-  o.w = f2bf(s1.z) | ((uint32_t)f2bf(s1.w) << 16);
+  o.x = pack_bf16x2(s0.x, s0.y);
+  o.y = pack_bf16x2(s0.z, s0.w);
+  o.z = pack_bf16x2(s1.x, s1.y);
+  o.w = pack_bf16x2(s1.z, s1.w);
   *reinterpret_cast<u32x4*>(y + t * N + n) = o;
 }
 
@@ -663,7 +663,7 @@ __global__ __launch_bounds__(256) void expand_bf16_kernel(const uint8_t* blob, i
     for (int d = 0; d < 4; ++d) {
       const float lo = __builtin_fmaf(bf16lo(pr[d]) - 128.0f, sc[ct], bi[ct]);
       const float hi = __builtin_fmaf(bf16hi(pr[d]) - 128.0f, sc[ct], bi[ct]);
-      o[d] = (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+      o[d] = pack_bf16x2(lo, hi);
     }
     *reinterpret_cast<u32x4*>(ob + ((int64_t)q * 8 + wd) * 1024 + lane * 16) = u32x4{o[0], o[1], o[2], o[3]};
   }
