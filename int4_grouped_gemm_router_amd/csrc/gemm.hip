@@ -24,8 +24,9 @@
 //   acc += s * P + (b - 128 s) * xsum          (fp32 VALU)
 // Algebraically this is x . (q s + b) with the weights used exactly.
 //
-// Epilogues: gate/up -> h = silu(gate) * up rounded to bf16; down -> the
-// output in fp32 at [token][slot]; the combine kernel then forms
+// Epilogues: gate/up -> h = silu(gate) * up rounded to bf16; down -> a routed
+// row rounded to bf16 at its (token, slot) pair index, a shared-expert row in
+// fp32 at its token; the combine kernel then forms
 // y = bf16(shared + sum over the k slots of weight * output) in a fixed order,
 // so the result is deterministic.
 #include <atomic>

@@ -24,13 +24,14 @@ namespace moe {
 
 // ---------------------------------------------------------------- router
 
-// Grid: (ceil(T/(16 NW)), E/64, KS). Block: NW waves (4, or 8 for long
+// Grid: (ceil(T/(16 NW)), E/(16 CT), KS). Block: NW waves (4, or 8 for long
 // chunks, which halves how often the weight tile is re-read); wave w owns
-// tokens [16 NW bx + 16w, +16) and all 64 experts of the tile (4 MFMA tiles).
-// The three bf16 planes of the 64-expert weight tile (24 KB per 64-input
-// group) are shared by the waves: they arrive in a three-stage LDS ring by
-// asynchronous global -> LDS copies, 24 / NW 1 KB copies per wave per group;
-// the activation fragments arrive in a register ring alongside.
+// tokens [16 NW bx + 16w, +16) and all 16 CT experts of the block's tile (CT
+// MFMA tiles: 2 below 1024 tokens, which doubles the blocks, else 4).
+// The three bf16 planes of the weight tile (6 CT KB per 64-input group) are
+// shared by the waves: they arrive in a three-stage LDS ring by asynchronous
+// global -> LDS copies, 6 CT / NW 1 KB copies per wave per group; the
+// activation fragments arrive in a register ring alongside.
 constexpr int kRStages = 3;
 
 template <int LOADS>
