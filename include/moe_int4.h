@@ -57,6 +57,7 @@ extern "C" {
 #define MOE_EHIP (-4)         /* a HIP launch reported an error               */
 #define MOE_EBUFFER (-5)      /* host output buffer too small (packers)       */
 #define MOE_EFORMAT (-6)      /* int4 code outside 0..15                      */
+#define MOE_ESCRATCH (-7)     /* request exceeds the library's static scratch  */
 
 /* Layer dimensions: hidden size H, expert intermediate size I, routed experts
  * E, experts per token top_k, rows per routing block block_m. */
@@ -177,6 +178,26 @@ int moe_prefill_layer(const moe_dims* dims, const moe_layer_weights* w, const ui
 int moe_decode_layer(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x,
                      uint16_t* y, int32_t T, float* logits_out, const moe_route_out* route_out,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* moe_decode_layer for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments and results as moe_decode_layer without the workspace: the
+ * decode kernels' scratch (router logits, top-k, SwiGLU rows) lives in a
+ * static device array of MOE_NOALLOC_SCRATCH_BYTES bytes inside the library,
+ * one copy per GPU, held until the process ends. The call allocates and
+ * frees nothing (its first call on a device resolves that device's array
+ * address once with hipGetSymbolAddress; make that first call outside graph
+ * capture). Nothing in the array needs to start at zero: every call writes
+ * what it reads. Calls that overlap on one GPU (several streams, or several
+ * host threads) share the array and race: serialise them. Returns
+ * MOE_ESCRATCH if the request needs more scratch than the array holds (the
+ * supported dims with T <= 4 need at most 299,520 bytes), otherwise the
+ * codes of moe_decode_layer (MOE_EHIP also if the array's address cannot be
+ * resolved). */
+#define MOE_NOALLOC_SCRATCH_BYTES (320 * 1024)
+int moe_decode_layer_noalloc(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x,
+                             uint16_t* y, int32_t T, float* logits_out,
+                             const moe_route_out* route_out, void* stream);
 
 /* The prefill layer with host-synchronised routing, for measuring what
  * GPU-resident routing saves (diariobitcoin.com, "Perplexity libera Lily...",

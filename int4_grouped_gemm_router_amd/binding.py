@@ -19,6 +19,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "moe_int4.h")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_EBUFFER, MOE_EFORMAT = (
     0, -1, -2, -3, -4, -5, -6)
+MOE_ESCRATCH = -7
+NOALLOC_SCRATCH_BYTES = 320 * 1024
 MODE_PREFILL, MODE_DECODE, MODE_ROUTE = 0, 1, 2
 HEADER_BYTES = 256
 
@@ -89,6 +91,8 @@ def lib():
         L.moe_prefill_layer_unfused.argtypes = [P(MoeDims), P(MoeLayerWeights), _vp, _vp, _i32, _i32,
                                                 _vp, _sz, _vp, _sz, _vp]
         L.moe_decode_layer_profiled.argtypes = L.moe_decode_layer.argtypes + [_vp, _i32]
+        L.moe_decode_layer_noalloc.argtypes = [P(MoeDims), P(MoeLayerWeights), _vp, _vp, _i32, _vp,
+                                               P(MoeRouteOut), _vp]
         L.moe_ceiling_read.argtypes = [_vp, _sz, _vp, _vp]
         L.moe_ceiling_mfma.argtypes = [_i32, _vp, P(ctypes.c_double), _vp]
         L.moe_strerror.argtypes = [ctypes.c_int]
@@ -98,7 +102,8 @@ def lib():
                      "moe_prefill_layer", "moe_decode_layer", "moe_test_dequant",
                      "moe_prefill_layer_profiled", "moe_decode_layer_profiled",
                      "moe_prefill_layer_host_routed", "moe_unfused_weight_bytes",
-                     "moe_prefill_layer_unfused", "moe_ceiling_read", "moe_ceiling_mfma"):
+                     "moe_prefill_layer_unfused", "moe_ceiling_read", "moe_ceiling_mfma",
+                     "moe_decode_layer_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -316,6 +321,15 @@ def moe_decode_layer(d: MoeDims, w: DeviceWeights, x, y, T: int, logits_out=None
                                   _ptr(logits_out), ro, _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream(stream)),
            "moe_decode_layer")
+
+
+def moe_decode_layer_noalloc(d: MoeDims, w: DeviceWeights, x, y, T: int, logits_out=None,
+                             route_out: RouteBuffers | None = None, stream=None):
+    """moe_decode_layer on the library's static scratch (no workspace argument)."""
+    ro = ctypes.byref(route_out.struct) if route_out is not None else None
+    _check(lib().moe_decode_layer_noalloc(ctypes.byref(d), ctypes.byref(w.struct), _ptr(x), _ptr(y), T,
+                                          _ptr(logits_out), ro, _stream(stream)),
+           "moe_decode_layer_noalloc")
 
 
 def _event_array(events):

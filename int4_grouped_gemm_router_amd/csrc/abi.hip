@@ -1,6 +1,7 @@
 // C ABI of the int4 MoE library: argument checks, workspace carve-up, the
 // chunk loop, and the launches on the caller's stream (include/moe_int4.h).
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 
 #include "../../include/moe_int4.h"
@@ -159,6 +160,8 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
 int decode_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x, uint16_t* y,
                 int32_t T, float* logits_out, const moe_route_out* route_out, void* ws,
                 size_t ws_bytes, void* stream, hipEvent_t* ev);
+int decode_args(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x, uint16_t* y,
+                int32_t T, float* logits_out, const moe_route_out* route_out);
 
 }  // namespace
 
@@ -456,17 +459,27 @@ int moe_decode_layer_profiled(const moe_dims* dims, const moe_layer_weights* w, 
 
 namespace {
 
-int decode_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x, uint16_t* y,
-                int32_t T, float* logits_out, const moe_route_out* route_out, void* ws,
-                size_t ws_bytes, void* stream, hipEvent_t* ev) {
+// Checks of the decode arguments other than the workspace (MOE_OK: valid,
+// T > 0).
+int decode_args(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x, uint16_t* y,
+                int32_t T, float* logits_out, const moe_route_out* route_out) {
   if (!dims || T < 0) return MOE_EINVAL;
   if (!dims_ok(dims) || T > kDecodeMaxT) return MOE_EUNSUPPORTED;
   if (T == 0) return MOE_OK;
-  if (!w || !x || !y || !ws || !w->router_w || !w->experts_gate_up || !w->experts_down ||
+  if (!w || !x || !y || !w->router_w || !w->experts_gate_up || !w->experts_down ||
       !w->shared_gate_up || !w->shared_down)
     return MOE_EINVAL;
   if (route_out && !route_out_ok(route_out)) return MOE_EINVAL;
-  if (!al16(x) || !al16(y) || !al16(ws) || !al4(logits_out) || !weights_aligned(w)) return MOE_EINVAL;
+  if (!al16(x) || !al16(y) || !al4(logits_out) || !weights_aligned(w)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int decode_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x, uint16_t* y,
+                int32_t T, float* logits_out, const moe_route_out* route_out, void* ws,
+                size_t ws_bytes, void* stream, hipEvent_t* ev) {
+  const int rc = decode_args(dims, w, x, y, T, logits_out, route_out);
+  if (rc != MOE_OK || T == 0) return rc;
+  if (!ws || !al16(ws)) return MOE_EINVAL;
   size_t need;
   carve_decode(dims, T, nullptr, &need);
   if (ws_bytes < need) return MOE_EWORKSPACE;
@@ -507,7 +520,48 @@ int decode_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_t
 
 }  // namespace
 
+// Scratch of moe_decode_layer_noalloc: a file-scope device array, one copy
+// per GPU. Host code never passes `scratch` itself to a kernel (on the host
+// it names a stand-in, not a device address); it uses the per-device address
+// from hipGetSymbolAddress below.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the current device, resolved once per device
+// with that device current. Concurrent first calls may both resolve it and
+// store the same value. Null if the address cannot be resolved.
+void* scratch_address() {
+  static std::atomic<void*> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = cached[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    cached[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+
+}  // namespace
+
 extern "C" {
+
+int moe_decode_layer_noalloc(const moe_dims* dims, const moe_layer_weights* w, const uint16_t* x,
+                             uint16_t* y, int32_t T, float* logits_out,
+                             const moe_route_out* route_out, void* stream) {
+  const int rc = decode_args(dims, w, x, y, T, logits_out, route_out);
+  if (rc != MOE_OK || T == 0) return rc;
+  size_t need = 0;
+  carve_decode(dims, T, nullptr, &need);
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ESCRATCH;
+  void* ws = scratch_address();
+  if (!ws) return MOE_EHIP;
+  return decode_impl(dims, w, x, y, T, logits_out, route_out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream,
+                     nullptr);
+}
 
 const char* moe_strerror(int code) {
   switch (code) {
@@ -518,6 +572,7 @@ const char* moe_strerror(int code) {
     case MOE_EHIP: return "HIP launch error";
     case MOE_EBUFFER: return "output buffer too small";
     case MOE_EFORMAT: return "int4 code outside 0..15";
+    case MOE_ESCRATCH: return "request exceeds the static scratch of the no-allocation entry point";
     default: return "unknown error";
   }
 }

@@ -213,3 +213,31 @@ def test_workspace_and_block_bounds():
     # the down outputs dominate: k*T*H bf16 routed rows + T*H fp32 shared rows
     assert b >= 8 * 4096 * 2048 * 2 + 4096 * 2048 * 4
     assert B.moe_workspace_bytes(d, 4, B.MODE_DECODE) > 0
+
+
+def test_noalloc_decode_rejects_bad_arguments():
+    # the no-allocation decode entry point checks its arguments before it
+    # touches the device (its scratch address is resolved only for valid calls)
+    L = B.lib()
+    d = B.dims(2048, 512)
+    by = ctypes.byref
+    w = B.MoeLayerWeights(*([FAKE] * 7))
+    f = L.moe_decode_layer_noalloc
+    assert f(by(d), by(w), FAKE, FAKE, 0, None, None, None) == B.MOE_OK
+    assert f(by(d), by(w), FAKE, FAKE, -1, None, None, None) == B.MOE_EINVAL
+    assert f(by(d), by(w), FAKE, FAKE, 5, None, None, None) == B.MOE_EUNSUPPORTED
+    assert f(by(B.dims(2048, 512, top_k=4)), by(w), FAKE, FAKE, 1, None, None, None) == B.MOE_EUNSUPPORTED
+    assert f(by(d), by(w), None, FAKE, 1, None, None, None) == B.MOE_EINVAL
+    assert f(by(d), by(w), FAKE + 4, FAKE, 1, None, None, None) == B.MOE_EINVAL
+    assert f(by(d), None, FAKE, FAKE, 1, None, None, None) == B.MOE_EINVAL
+    assert B.strerror(B.MOE_ESCRATCH).startswith("request exceeds the static scratch")
+
+
+def test_noalloc_scratch_covers_every_supported_decode():
+    # the static scratch is stated in the header; every supported decode call
+    # (T <= 4, E <= 256, I <= 4096) fits in it, the largest needing 299,520 bytes
+    hdr = open(B.HEADER).read()
+    assert "#define MOE_NOALLOC_SCRATCH_BYTES (320 * 1024)" in hdr
+    need = max(B.moe_workspace_bytes(B.dims(H, I, E), T, B.MODE_DECODE)
+               for H in (256, 4096) for I in (128, 4096) for E in (64, 256) for T in (1, 4))
+    assert need == 299520 <= B.NOALLOC_SCRATCH_BYTES
