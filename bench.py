@@ -88,7 +88,7 @@ def _graph_of(calls):
     return g
 
 
-def run_prefill(name, steps, warmup, copies, chunk=None, block_m=32):
+def run_prefill(name, steps, warmup, copies, chunk=None, block_m=32, gemm=0):
     """Time `steps` layer calls. The step time (value) comes from replaying a
     HIP graph of `copies` consecutive layer calls (one per weight copy); the
     per-kernel durations come from HIP events recorded on the library's
@@ -97,7 +97,7 @@ def run_prefill(name, steps, warmup, copies, chunk=None, block_m=32):
     from int4_grouped_gemm_router_amd import binding as B
     wl, w, x, xd, dws = prefill_setup(name, copies)
     d0 = dws[0].dims
-    d = B.dims(d0.H, d0.I, d0.E, d0.top_k, block_m)
+    d = B.dims(d0.H, d0.I, d0.E, d0.top_k, block_m, gemm)
     T, H, I = wl.T, wl.H, wl.I
     chunk = wl.chunk if chunk is None else chunk
     Tc = chunk if chunk else T

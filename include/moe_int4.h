@@ -32,9 +32,10 @@
  *    16-byte vectors); logits, logits_out, router_bias and the route_out
  *    arrays 4-byte aligned. Misaligned pointers give MOE_EINVAL. (Fresh
  *    torch / hipMalloc allocations are 256-byte aligned.)
- *  - Supported dims: E <= 256 and E % 64 == 0, top_k == 8, block_m 32 or 16
- *    (the routing block size, which is also the row count of the grouped
- *    GEMMs' work items; diariobitcoin.com, "Perplexity libera Lily...",
+ *  - Supported dims: E <= 256 and E % 64 == 0, top_k == 8, gemm one of
+ *    MOE_GEMM_*, block_m 32 or 16
+ *    (the routing block size, which is also the row count of the exact
+ *    grouped GEMMs' work items; diariobitcoin.com, "Perplexity libera Lily...",
  *    section "Las optimizaciones en el prefill": 32-row blocks replaced
  *    16-row ones), H % 256 == 0 (H <= 4096), I % 128 == 0
  *    (I <= 4096), and T * top_k < 2^30 tokens x slots per call (pair
@@ -60,9 +61,29 @@ extern "C" {
 #define MOE_ESCRATCH (-7)     /* request exceeds the library's static scratch  */
 
 /* Layer dimensions: hidden size H, expert intermediate size I, routed experts
- * E, experts per token top_k, rows per routing block block_m. */
+ * E, experts per token top_k, rows per routing block block_m, and which
+ * grouped-GEMM kernels the prefill uses (gemm, one of MOE_GEMM_*):
+ *   MOE_GEMM_EXACT  work items of block_m rows; the int4 codes enter the
+ *                   matrix cores as exact bf16 values 128 + q and scale and
+ *                   bias are applied per output and group in fp32 (weights
+ *                   used exactly); suited to short chunks, where few rows
+ *                   share an expert and the layer streams weights from HBM;
+ *   MOE_GEMM_WIDE   work items of up to 128 rows of one expert; each weight
+ *                   is expanded once per item to bf16 w = q*scale + bias
+ *                   (fp32 value rounded once to bf16) and the matrix cores
+ *                   accumulate x.w in fp32; suited to long chunks, where many
+ *                   rows share each expanded weight;
+ *   MOE_GEMM_AUTO   (0) WIDE for chunks whose pairs average at least 32 rows
+ *                   per expert (top_k * T_chunk >= 32 * E), else EXACT.
+ * (diariobitcoin.com, "Perplexity libera Lily...", section "Las
+ * optimizaciones en el prefill": the grouped GEMM reconstructs the 4-bit
+ * weights block by block on chip with fp32 accumulation.) Decode ignores
+ * gemm. */
+#define MOE_GEMM_AUTO 0
+#define MOE_GEMM_EXACT 1
+#define MOE_GEMM_WIDE 2
 typedef struct {
-  int32_t H, I, E, top_k, block_m;
+  int32_t H, I, E, top_k, block_m, gemm;
 } moe_dims;
 
 /* Device weights of one layer. Every pointer is a device pointer. The blobs
@@ -159,8 +180,9 @@ int moe_route(const moe_dims* dims, const float* logits, int32_t T, const moe_ro
  * en el prefill": long prompts run in bounded chunks). logits_out (device
  * [T][E] fp32) receives the router logits when non-null. route_out, when
  * non-null, receives the routing metadata of the LAST chunk (sized for that
- * chunk's token count). Numerics: fp32 router logits; int4 codes are expanded
- * exactly to bf16 on chip, scale and bias applied in fp32; fp32 accumulation;
+ * chunk's token count). Numerics: fp32 router logits; int4 weights expanded
+ * on chip as dims->gemm states (exact codes with fp32 scale and bias, or
+ * bf16 weights rounded once); fp32 accumulation;
  * the SwiGLU product h is rounded to bf16 before the down projection; each
  * of the k routed down outputs is rounded to bf16 (it enters with a routing
  * weight of about 1/k), the shared expert's stays fp32, and they are summed

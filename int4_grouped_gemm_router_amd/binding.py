@@ -22,6 +22,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_EBUFFER, MOE
 MOE_ESCRATCH = -7
 NOALLOC_SCRATCH_BYTES = 320 * 1024
 MODE_PREFILL, MODE_DECODE, MODE_ROUTE = 0, 1, 2
+GEMM_AUTO, GEMM_EXACT, GEMM_WIDE = 0, 1, 2
 HEADER_BYTES = 256
 
 _i32 = ctypes.c_int32
@@ -31,7 +32,8 @@ _sz = ctypes.c_size_t
 
 
 class MoeDims(ctypes.Structure):
-    _fields_ = [("H", _i32), ("I", _i32), ("E", _i32), ("top_k", _i32), ("block_m", _i32)]
+    _fields_ = [("H", _i32), ("I", _i32), ("E", _i32), ("top_k", _i32), ("block_m", _i32),
+                ("gemm", _i32)]
 
 
 class MoeLayerWeights(ctypes.Structure):
@@ -118,8 +120,8 @@ def _check(code, what):
         raise MoeError(code, what)
 
 
-def dims(H, I, E=256, top_k=8, block_m=32) -> MoeDims:
-    return MoeDims(H, I, E, top_k, block_m)
+def dims(H, I, E=256, top_k=8, block_m=32, gemm=GEMM_AUTO) -> MoeDims:
+    return MoeDims(H, I, E, top_k, block_m, gemm)
 
 
 def _ptr(t):

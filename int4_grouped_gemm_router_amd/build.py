@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libmoe_int4.so")
-SOURCES = ["abi.hip", "route.hip", "gemm.hip", "decode.hip", "pack.hip", "ceiling.hip"]
+SOURCES = ["abi.hip", "route.hip", "gemm.hip", "gemm_wide.hip", "decode.hip", "pack.hip", "ceiling.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -14,7 +14,19 @@ namespace {
 bool dims_ok(const moe_dims* d) {
   return d && d->E > 0 && d->E <= 256 && d->E % 64 == 0 && d->top_k == 8 && (d->block_m == 32 || d->block_m == 16) &&
          d->H > 0 && d->H % 256 == 0 && d->H <= 4096 && d->I > 0 && d->I % 128 == 0 &&
-         d->I <= 4096;
+         d->I <= 4096 && d->gemm >= MOE_GEMM_AUTO && d->gemm <= MOE_GEMM_WIDE;
+}
+
+// Wide GEMMs (items of up to kWideRows rows, bf16 weights expanded once per
+// item) when the chunk's pairs average at least kWideMinRows rows per expert:
+// then enough rows share each expanded weight for the matrix cores to set
+// the pace; below it the layer streams weights and the exact kernels' short
+// items spread them over more compute units.
+constexpr int kWideMinRows = 32;
+bool use_wide(const moe_dims* d, int Tn) {
+  if (d->gemm == MOE_GEMM_EXACT) return false;
+  if (d->gemm == MOE_GEMM_WIDE) return true;
+  return (int64_t)d->top_k * Tn >= (int64_t)kWideMinRows * d->E;
 }
 
 int64_t max_blocks(const moe_dims* d, int T) {
@@ -349,10 +361,18 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
     sa.E = E;
     sa.k = k;
     sa.block_m = dims->block_m;
-    sa.item_rows = dims->block_m;  // one GEMM work item per routing block
+    // GEMM work items: one per routing block (exact kernels), or up to
+    // kWideRows rows of one expert (wide kernels; not for the unfused path)
+    const bool wide = !unfused_w && use_wide(dims, Tn);
+    const int item_rows = wide ? kWideRows : dims->block_m;
+    sa.item_rows = item_rows;
+    sa.longest_first = wide ? 1 : 0;
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;
     if (launch_scan_scatter(sa, s) != hipSuccess) return MOE_EHIP;
 
+    const int shared_slots = (Tn + item_rows - 1) / item_rows;
+    // work-list slots the wide grids cover (an upper bound on the device's count)
+    int wide_slots = max_items(dims, Tn) + shared_slots;
     // host-routed variant: the host waits for the routing, reads the work
     // item count and launches exact grids (one block per 256-column unit)
     int gu_blocks = 0, dn_blocks = 0;
@@ -361,16 +381,17 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
       if (hipMemcpyAsync(&ni, W.num_items, sizeof ni, hipMemcpyDeviceToHost, s) != hipSuccess ||
           hipStreamSynchronize(s) != hipSuccess)
         return MOE_EHIP;
-      const int slots = ni + (Tn + dims->block_m - 1) / dims->block_m;
+      const int slots = ni + shared_slots;
       gu_blocks = std::max(1, slots * ((gu.n_wt + 3) / 4));
       dn_blocks = std::max(1, slots * ((dn.n_wt + 3) / 4));
+      wide_slots = slots;
     }
 
     GemmArgs g{};
     g.items = W.items;
     g.num_items = W.num_items;
-    g.item_rows = dims->block_m;
-    g.shared_slots = (Tn + g.item_rows - 1) / g.item_rows;
+    g.item_rows = item_rows;
+    g.shared_slots = shared_slots;
     g.T = Tn;
     g.k = k;
     g.perm = sa.perm;
@@ -403,7 +424,9 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
     g.act = xc;
     g.h_out = W.h;
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;
-    if (launch_gemm(kGateUp, g, s, gu_blocks) != hipSuccess) return MOE_EHIP;
+    if ((wide ? launch_gemm_wide(kGateUp, g, wide_slots, s) : launch_gemm(kGateUp, g, s, gu_blocks)) !=
+        hipSuccess)
+      return MOE_EHIP;
 
     // down: routed items (one output row per pair) and shared items in one launch
     g.blob = static_cast<const uint8_t*>(w->experts_down) + kHeaderBytes;
@@ -425,7 +448,9 @@ int prefill_impl(const moe_dims* dims, const moe_layer_weights* w, const uint16_
     g.partial_r = W.partial_r;
     g.partial_s = W.partial_s;
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;
-    if (launch_gemm(kDown, g, s, dn_blocks) != hipSuccess) return MOE_EHIP;
+    if ((wide ? launch_gemm_wide(kDown, g, wide_slots, s) : launch_gemm(kDown, g, s, dn_blocks)) !=
+        hipSuccess)
+      return MOE_EHIP;
 
     // y = bf16(shared + sum of the k weighted expert outputs)
     if (rec.mark(s) != hipSuccess) return MOE_EHIP;

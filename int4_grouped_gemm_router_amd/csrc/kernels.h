@@ -12,6 +12,7 @@ namespace moe {
 
 constexpr int kChunkPairs = 1024;  // (token, slot) pairs per scatter block
 constexpr int kItemRows = 32;      // most rows of one expert per GEMM work item (one routing block)
+constexpr int kWideRows = 128;     // rows per work item of the wide GEMMs
 constexpr int kMaxGroups = 64;     // K / 64 upper bound of the expert GEMMs
 constexpr int kDecodeMaxT = 4;
 constexpr int kMaxSplits = 8;      // router K splits summed by the top-k kernel
@@ -33,7 +34,10 @@ struct ScatterArgs {
   int32_t *hist, *offsets, *perm, *inv_perm, *block_map, *num_blocks;
   int32_t *items, *num_items;  // GEMM work list or null
   int T, E, k, block_m;
-  int item_rows;               // rows per GEMM work item (<= kItemRows)
+  int item_rows;               // rows per GEMM work item
+  int longest_first;           // 1: the work list holds every expert's full items
+                               // (expert order), then the experts' last partial
+                               // items, larger first (ties: lower expert)
 };
 
 // Which GEMM: gate/up with SwiGLU, or down (routed and shared items) writing
@@ -69,6 +73,11 @@ hipError_t launch_fill_zero(int* p, int n, hipStream_t s);
 // grid_blocks > 0: that many blocks (rounded up to a multiple of 8) instead
 // of the persistent grid (used when the host knows the exact unit count).
 hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t s, int grid_blocks = 0);
+// The wide GEMMs (items of up to kWideRows rows, weights expanded to bf16
+// once per item): a.items / a.num_items hold kWideRows-row items and
+// a.shared_slots counts kWideRows-token shared items; max_slots bounds
+// items + shared items (the grid is sized from it, extra blocks exit).
+hipError_t launch_gemm_wide(GemmMode mode, const GemmArgs& a, int max_slots, hipStream_t s);
 // y[t][n] = bf16(shared[t][n] + sum_{j<k} topk_w[t][j] * routed[t*k + j][n]) (j ascending).
 hipError_t launch_combine(const uint16_t* routed, const float* shared, const float* topk_w, uint16_t* y,
                           int T, int N, int k, hipStream_t s);

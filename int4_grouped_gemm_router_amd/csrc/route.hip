@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256) void scan_scatter_kernel(ScatterArgs a) {
     }
     if (tid == 0) *a.num_blocks = nb_total;
     // GEMM work items: up to item_rows rows of one expert
-    if (a.items) {
+    if (a.items && !a.longest_first) {
       int ni_total;
       const int ir = a.item_rows;
       const int ni = tid < E ? (tot + ir - 1) / ir : 0;
@@ -262,6 +262,51 @@ __global__ __launch_bounds__(256) void scan_scatter_kernel(ScatterArgs a) {
         it[2] = min(ir, tot - i * ir);
       }
       if (tid == 0) *a.num_items = ni_total;
+    } else if (a.items) {
+      // full items first, then each expert's partial last item, larger
+      // first: blocks are handed out in work-list order, so the short items
+      // fill the end of the launch (longest-processing-time-first order)
+      int nf_total;
+      const int ir = a.item_rows;
+      const int nf = tid < E ? tot / ir : 0;
+      const int rem = tid < E ? tot - nf * ir : 0;
+      const int foff = block_exclusive_scan(nf, scratch, nf_total);
+      for (int i = 0; i < nf; ++i) {
+        int* it = a.items + 3 * (int64_t)(foff + i);
+        it[0] = tid;
+        it[1] = off + i * ir;
+        it[2] = ir;
+      }
+      // rank among the partial items (remainder sizes 1 .. ir - 1 < 256):
+      // a counting sort, larger first, equal sizes by expert index. Per wave,
+      // ballot matching finds the lanes with the same size; wbase (not yet in
+      // use) holds each wave's count per size, then the counts of all sizes
+      // above each size.
+      int* rcnt = &wbase[0][0];                 // [4 waves][256 sizes]
+      for (int i = tid; i < 4 * 256; i += 256) rcnt[i] = 0;
+      __syncthreads();
+      const uint64_t peers = match_any((uint32_t)rem, 8);
+      const int wrank = __popcll(peers & lanemask_lt());
+      if (rem > 0 && wrank == 0) rcnt[wave * 256 + rem] = __popcll(peers);
+      __syncthreads();
+      int before_w = 0;
+      for (int w = 0; w < 4; ++w) before_w += w < wave ? rcnt[w * 256 + rem] : 0;
+      const int b = 255 - tid;                  // sizes in descending order
+      const int cb = b >= 1 ? rcnt[b] + rcnt[256 + b] + rcnt[512 + b] + rcnt[768 + b] : 0;
+      int nrem;
+      const int above = block_exclusive_scan(cb, scratch, nrem);
+      off_s[b] = above;                         // items of sizes larger than b
+      __syncthreads();
+      if (rem > 0) {
+        const int rank = off_s[rem] + before_w + wrank;
+        int* it = a.items + 3 * (int64_t)(nf_total + rank);
+        it[0] = tid;
+        it[1] = off + nf * ir;
+        it[2] = rem;
+      }
+      if (tid == 0) *a.num_items = nf_total + nrem;
+      __syncthreads();
+      if (tid < E) off_s[tid] = off;
     }
   }
   // wave-level counts of this chunk's pairs: wave w owns 256 consecutive pairs

@@ -154,7 +154,8 @@ def test_entry_points_reject_bad_arguments():
                               None) == B.MOE_EWORKSPACE
     assert L.moe_test_dequant(FAKE, 2, 64, 64, 0, 2, FAKE, None) == B.MOE_EINVAL
     for dd in (B.dims(2048, 512, E=320), B.dims(2000, 512), B.dims(2048, 100),
-               B.dims(2048, 512, block_m=24), B.dims(2048, 512, block_m=64)):
+               B.dims(2048, 512, block_m=24), B.dims(2048, 512, block_m=64),
+               B.dims(2048, 512, gemm=3), B.dims(2048, 512, gemm=-1)):
         n = ctypes.c_size_t(0)
         assert L.moe_workspace_bytes(by(dd), 64, 0, by(n)) == B.MOE_EUNSUPPORTED
     assert B.strerror(B.MOE_EWORKSPACE) == "workspace too small"

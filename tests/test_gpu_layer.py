@@ -38,8 +38,8 @@ def _layer(name, seed=0):
     return _cache[key]
 
 
-def _prefill(torch, dw, x, chunk=0, route=True):
-    d = dw.dims
+def _prefill(torch, dw, x, chunk=0, route=True, d=None):
+    d = dw.dims if d is None else d
     T = x.shape[0]
     xd = torch.from_numpy(x).cuda()
     y = torch.empty((T, d.H), dtype=torch.int16, device="cuda")
@@ -149,7 +149,9 @@ def test_prefill_unfused_matches_oracle(torch_cuda):
         print(f"unfused {name} T={T}: {s}")
 
 
-def test_prefill_skew_t2048_sampled(torch_cuda):
+def test_prefill_skew_t2048_all_tokens(torch_cuda):
+    # the Zipf-skewed workload (automatic choice: the wide 128-row GEMMs),
+    # every token against the oracle
     wl, w, dw = _layer("skew_t2048")
     _, _, x = synth.generate("skew_t2048", with_x=True)
     T = x.shape[0]
@@ -158,21 +160,18 @@ def test_prefill_skew_t2048_sampled(torch_cuda):
     check_route_meta(meta, idx, 256, 8, 32)
     hist = meta["hist"]
     assert (hist == 0).sum() > 50 and hist.max() > 500, "skewed routing expected"
-    # sample: the first 64 tokens, 64 spread tokens, and 64 tokens of the heaviest expert
-    heavy = int(np.argmax(hist))
-    heavy_tokens = np.nonzero((idx == heavy).any(axis=1))[0]
-    sample = np.unique(np.concatenate([np.arange(64), np.linspace(0, T - 1, 64).astype(int),
-                                       heavy_tokens[:: max(1, len(heavy_tokens) // 64)][:64]]))
-    s = check_layer(x, w, y, logits, idx, wsel, tokens=sample)
-    print(f"skew T=2048 ({len(sample)} sampled): {s}")
+    s = check_layer(x, w, y, logits, idx, wsel)
+    print(f"skew T=2048 (all {T} tokens): {s}", flush=True)
     # the same prompt in 512-token chunks (64-token router tiles instead of
-    # 128-token ones): identical logits and outputs
+    # 128-token ones, exact 32-row GEMMs instead of wide ones): identical
+    # logits, and outputs within the bar of the oracle
     y2, logits2, _ = _prefill(torch_cuda, dw, x, chunk=512, route=False)
     assert np.array_equal(logits, logits2)
-    assert np.array_equal(y, y2)
+    s2 = check_layer(x, w, y2, logits2, idx, wsel)
+    print(f"skew T=2048 in 512-token chunks: {s2}", flush=True)
 
 
-def test_prefill_long_chunked_sampled(torch_cuda):
+def test_prefill_long_chunked_all_tokens(torch_cuda):
     wl, w, dw = _layer("prefill_t512")   # same layer shape as the long prompt
     x = synth.make_x(np.random.default_rng(16384), 16384, w.H)
     y, logits, meta = _prefill(torch_cuda, dw, x, chunk=4096)
@@ -183,8 +182,6 @@ def test_prefill_long_chunked_sampled(torch_cuda):
     y1, logits1, _ = _prefill(torch_cuda, dw, x, chunk=0, route=False)
     assert np.array_equal(y, y1), "chunked and unchunked outputs differ"
     assert np.array_equal(logits, logits1)
-    sample = np.unique(np.concatenate([np.arange(0, T, 128), np.arange(4090, 4100),
-                                       np.arange(T - 16, T)]))
     # the GPU's selections for every token, from its own logits via moe_route
     torch = torch_cuda
     d = dw.dims
@@ -193,8 +190,55 @@ def test_prefill_long_chunked_sampled(torch_cuda):
     torch.cuda.synchronize()
     idx_all, w_all = _route_of(ro.to_numpy(), T)
     assert np.array_equal(idx_all[-4096:], idx_last)
-    s = check_layer(x, w, y, logits, idx_all, w_all, tokens=sample)
-    print(f"long T=16384 chunk 4096 ({len(sample)} sampled): {s}")
+    s = check_layer(x, w, y, logits, idx_all, w_all)
+    print(f"long T=16384 chunk 4096 (all {T} tokens): {s}", flush=True)
+
+
+@pytest.mark.parametrize("T", [1, 5, 100, 300])
+def test_prefill_wide_tiny_all_tokens(torch_cuda, T):
+    # the wide GEMMs (items of up to 128 rows, bf16 weights expanded once per
+    # item) forced on the tiny layer: one gate/up and two down column tiles,
+    # 8 and 2 groups, ragged items and shared items
+    wl, w, dw = _layer("tiny_t32")
+    d = B.dims(w.H, w.I, gemm=B.GEMM_WIDE)
+    x = synth.make_x(np.random.default_rng(500 + T), T, w.H)
+    y, logits, meta = _prefill(torch_cuda, dw, x, d=d)
+    idx, wsel = _route_of(meta, T)
+    check_route_meta(meta, idx, 256, 8, 32)
+    s = check_layer(x, w, y, logits, idx, wsel)
+    print(f"wide tiny T={T}: {s}", flush=True)
+
+
+def test_prefill_wide_forced_heavy_routing(torch_cuda):
+    # twelve experts take nearly every pair: items of 128 rows plus ragged
+    # tails, 244 empty experts; wide and exact GEMMs both against the oracle
+    import copy
+    _, w, _ = _layer("tiny_t32")
+    w2 = copy.deepcopy(w)
+    rb = np.zeros(256, np.float32)
+    rb[:8] = 6.0
+    rb[100:104] = 5.9
+    w2.router_bias = rb
+    dw2 = B.DeviceWeights.from_logical(w2)
+    x = synth.make_x(np.random.default_rng(4), 700, w.H)
+    for gemm in (B.GEMM_WIDE, B.GEMM_EXACT):
+        y, logits, meta = _prefill(torch_cuda, dw2, x, d=B.dims(w.H, w.I, gemm=gemm))
+        idx, wsel = _route_of(meta, 700)
+        check_route_meta(meta, idx, 256, 8, 32)
+        assert (meta["hist"] == 0).sum() >= 200 and meta["hist"].max() > 300
+        s = check_layer(x, w2, y, logits, idx, wsel)
+        print(f"forced heavy routing, gemm {gemm}: {s}", flush=True)
+
+
+def test_prefill_wide_t512_all_tokens(torch_cuda):
+    # the 512-token layer with the wide GEMMs forced (about 16 rows per
+    # expert): every token against the oracle
+    wl, w, dw = _layer("prefill_t512")
+    _, _, x = synth.generate("prefill_t512", with_x=True)
+    y, logits, meta = _prefill(torch_cuda, dw, x, d=B.dims(w.H, w.I, gemm=B.GEMM_WIDE))
+    idx, wsel = _route_of(meta, 512)
+    s = check_layer(x, w, y, logits, idx, wsel)
+    print(f"wide T=512: {s}", flush=True)
 
 
 def test_prefill_ragged_chunks(torch_cuda):
