@@ -22,6 +22,8 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   ceilings      measured on this device in the same run: streaming HBM read
                 GB/s over a 2 GiB buffer and the bf16 MFMA loop's TFLOP/s
   cpu_baseline  the CPU oracle timed on this host on the same workload
+  roofline_mfma the matrix-core roofline (gate/up and down kernels, and the
+                whole layer's expert flops) of the two long-chunk workloads
   secondary     the 2048-token Zipf-skewed prefill (bf16 MFMA fraction), the
                 16384-token prompt in 4096-token chunks, and batch-1 and
                 batch-4 decode (HBM GB/s of the GEMV kernels), same method
@@ -156,6 +158,18 @@ def run_prefill(name, steps, warmup, copies, chunk=None, block_m=32, gemm=0):
     res["mfma_frac_layer"] = res["expert_tflops"] / PEAK_BF16_TFLOPS
     gu_ms = float(kern_ms[3])
     res["gateup_tflops"] = gate_up_flops / (gu_ms / 1e3) / 1e12
+    dn_ms = float(kern_ms[4])
+    down_flops = 2.0 * (wl.k + 1) * Tc * H * I
+    res["down_tflops"] = down_flops / (dn_ms / 1e3) / 1e12
+    # matrix-core roofline of the gate/up kernel (algorithmic flops per launch
+    # over its mean launch duration; HIP events on the library's stream)
+    res["roofline_gateup"] = {"bound": "mfma", "achieved": res["gateup_tflops"], "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": res["gateup_tflops"] / PEAK_BF16_TFLOPS,
+                              "kernel": "gemm_gateup", "per_launch_flops": gate_up_flops,
+                              "mean_us": gu_ms * 1e3}
+    res["roofline_down"] = {"bound": "mfma", "achieved": res["down_tflops"], "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": res["down_tflops"] / PEAK_BF16_TFLOPS,
+                            "kernel": "gemm_down", "per_launch_flops": down_flops, "mean_us": dn_ms * 1e3}
     if U is not None:
         gu_bytes = (U + 1) * gu_b + T * H * 2 + (wl.k + 1) * T * I * 2
         res["touched_experts"] = U
@@ -230,6 +244,18 @@ def run_decode(name, steps, warmup, copies):
                 end_to_end_gbs=(gemv_bytes + router_bytes) / (ms_step / 1e3) / 1e9)
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, x, min_seconds=10.0):
     """The CPU oracle on the same workload: whole passes over all T tokens,
     repeated until at least `min_seconds` have elapsed."""
@@ -244,6 +270,7 @@ def cpu_baseline(w, x, min_seconds=10.0):
         if dt >= min_seconds:
             break
     return {"value": passes * T / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+            "cpu_model": cpu_model(),
             "kind": "oracle", "sample": f"{passes} full pass(es) over the {T} tokens of the same "
             f"workload (router, top-8, 8 routed + shared SwiGLU experts, fp64 accumulation), "
             f"{dt:.1f} s wall"}
@@ -473,6 +500,11 @@ def main():
             if "gemv_gbs" in r:
                 r["hbm_frac_of_measured"] = r["gemv_gbs"] / ceil["hbm_read_gbs"]
         out["secondary"] = sec
+        # matrix-core rooflines of the long-chunk configurations (the bf16
+        # peak-fraction half of the metric), beside the HBM one above
+        out["roofline_mfma"] = {r["workload"]: {"gate_up": r["roofline_gateup"], "down": r["roofline_down"],
+                                                "layer_frac": r["mfma_frac_layer"]}
+                                for r in (r2, r4)}
     print(json.dumps(out), flush=True)
 
 

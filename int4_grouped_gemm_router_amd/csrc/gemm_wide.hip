@@ -287,7 +287,11 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(GemmArgs a) {
       step(g + 1, I1{});
     }
   };
-  if (nsub <= 4)
+  if (nsub <= 1)
+    run(std::integral_constant<int, 1>{});
+  else if (nsub <= 2)
+    run(std::integral_constant<int, 2>{});
+  else if (nsub <= 4)
     run(std::integral_constant<int, 4>{});
   else if (nsub <= 6)
     run(std::integral_constant<int, 6>{});

@@ -116,18 +116,22 @@ def test_prefill_t512_block16(torch_cuda):
 
 def test_prefill_host_routed_matches(torch_cuda):
     # the host-synchronised routing variant launches exact grids; every unit
-    # is computed the same way, so y equals the GPU-routed call bit for bit
+    # is computed the same way, so y equals the GPU-routed call bit for bit,
+    # and on its own inputs it meets the oracle bar (every token)
     torch = torch_cuda
     for name, T in (("prefill_t512", 512), ("skew_t2048", 2048), ("tiny_t32", 37)):
         wl, w, dw = _layer(name)
         x = synth.make_x(np.random.default_rng(T), T, w.H)
-        y_ref, _, _ = _prefill(torch, dw, x, route=False)
+        y_ref, logits, meta = _prefill(torch, dw, x)
         d = dw.dims
         y = torch.empty((T, d.H), dtype=torch.int16, device="cuda")
         B.moe_prefill_layer_host_routed(d, dw, torch.from_numpy(x).cuda(), y, T, 0,
                                         B.workspace(d, T, B.MODE_PREFILL))
         torch.cuda.synchronize()
-        assert np.array_equal(y.cpu().numpy().view(np.uint16), y_ref), name
+        y = y.cpu().numpy().view(np.uint16)
+        assert np.array_equal(y, y_ref), name
+        s = check_layer(x, w, y, logits, *_route_of(meta, T))
+        print(f"host-routed {name} T={T}: {s}", flush=True)
 
 
 def test_prefill_unfused_matches_oracle(torch_cuda):
@@ -465,6 +469,13 @@ def test_decode_graph_replay_matches_eager(torch_cuda, T):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         steps()
+    # the eager steps against the oracle on their own inputs
+    for i in range(3):
+        xi = xs[i].cpu().numpy()
+        got = ref[i][2]
+        s = check_layer(xi, w, ref[i][0].cpu().numpy().view(np.uint16), ref[i][1].cpu().numpy(),
+                        got["topk_idx"].reshape(T, 8), got["topk_w"].reshape(T, 8))
+        print(f"graph decode T={T} step {i}: {s}", flush=True)
     for rep in range(3):
         for y, l, r in zip(ys, lg, ro):
             y.zero_()
@@ -535,3 +546,23 @@ def test_ceiling_helpers_run():
     assert torch.count_nonzero(sink).item() == 0
     with pytest.raises(B.MoeError):
         B.moe_ceiling_read(buf[:15], sink)  # not a multiple of 16 bytes
+
+
+# The exact 32-row GEMMs at family sizes whose down projection takes the
+# LDS-stream kernel (I / 64 not a multiple of 4: I = 384 and 640), on 8192
+# tokens: about 20 work units per persistent block, so the hand-off of copies
+# to the next unit and the rollover past a block's 16-unit batch both run.
+# Every token against the oracle; the wide kernels on the same inputs too
+# (their half-filled last column tile at I = 384 and 640).
+@pytest.mark.parametrize("H,I,E", [(1024, 384, 128), (768, 640, 192)])
+def test_exact_stream_kernel_long_run(torch_cuda, H, I, E):
+    rng = np.random.default_rng(H * 7 + I)
+    w = synth.make_weights(rng, H, I, E)
+    dw = B.DeviceWeights.from_logical(w)
+    T = 8192
+    x = synth.make_x(rng, T, H)
+    for gemm in (B.GEMM_EXACT, B.GEMM_WIDE):
+        y, logits, meta = _prefill(torch_cuda, dw, x, d=B.dims(H, I, E, gemm=gemm))
+        idx, wsel = _route_of(meta, T)
+        s = check_layer(x, w, y, logits, idx, wsel)
+        print(f"H={H} I={I} E={E} T={T} gemm {gemm}: {s}", flush=True)
