@@ -234,12 +234,15 @@ def run_decode(name, steps, warmup, copies):
     gu_b, dn_b = expert_bytes(H, I)
     gemv_bytes = (U + 1) * (gu_b + dn_b)
     router_bytes = wl.E * H * 4
-    gemv_ms = float(kern_ms[1] + kern_ms[2])
+    # the three decode kernels move the router matrix and the selected and
+    # shared experts' weights
+    gemv_ms = float(kern_ms[0] + kern_ms[1] + kern_ms[2])
     ms_step = wall * 1e3 / steps
     return dict(workload=name, T=T, steps=steps, ms_per_step=ms_step,
                 ms_per_step_eager=wall_eager * 1e3 / steps, graph_matches_eager=graph_ok,
                 unique_experts=U, kernels_us={k: float(v * 1e3) for k, v in zip(DECODE_KERNELS, kern_ms)},
-                gemv_bytes=gemv_bytes, gemv_gbs=gemv_bytes / (gemv_ms / 1e3) / 1e9,
+                gemv_bytes=gemv_bytes + router_bytes,
+                gemv_gbs=(gemv_bytes + router_bytes) / (gemv_ms / 1e3) / 1e9,
                 step_bytes=gemv_bytes + router_bytes,
                 end_to_end_gbs=(gemv_bytes + router_bytes) / (ms_step / 1e3) / 1e9)
 

@@ -365,6 +365,33 @@ def test_decode_skewed_router_bias(torch_cuda, T):
         assert min(uniq_counts) < 8 * T, "skewed routing should make tokens share experts"
 
 
+@pytest.mark.parametrize("T", [3, 4])
+def test_decode_all_distinct_experts(torch_cuda, T):
+    # router rows 8t..8t+7 read input dimension t strongly and token t alone
+    # carries that dimension, so the k*T pairs select k*T distinct experts:
+    # at T = 4 every routed slot is taken and the shared expert's gate/up
+    # tiles run after the last slot's own (at T = 3 it has a slot of its own)
+    import copy
+    _, w, _ = _layer("prefill_t512")
+    w2 = copy.deepcopy(w)
+    for t in range(T):
+        w2.router_w[8 * t:8 * t + 8, t] = 2.0
+    dw2 = B.DeviceWeights.from_logical(w2)
+    rng = np.random.default_rng(90 + T)
+    for step in range(2):
+        xf = synth.bf16_bits_to_f32(synth.make_x(rng, T, w.H))
+        xf[:, :T] = 0.0
+        for t in range(T):
+            xf[t, t] = 8.0
+        x = synth.f32_to_bf16_bits(xf)
+        y, logits, meta = _decode(torch_cuda, dw2, x)
+        idx, wsel = _route_of(meta, T)
+        assert np.array_equal(np.sort(idx, axis=1), np.arange(8 * T).reshape(T, 8))
+        assert meta["num_blocks"] == 8 * T
+        s = check_layer(x, w2, y, logits, idx, wsel)
+        print(f"all-distinct decode T={T} step {step}: {s}")
+
+
 def test_decode_tiny_and_vs_prefill(torch_cuda):
     _, w, dw = _layer("tiny_t32")
     x = synth.make_x(np.random.default_rng(11), 4, w.H)
