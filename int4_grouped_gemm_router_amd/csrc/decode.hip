@@ -414,8 +414,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_down_kernel(DecodeArgs a) 
   const int c16 = lane & 15, kb = lane >> 4;
   const int T = a.T, H = a.H, I = a.I;
   const PackGeom geom = pack_geom(H, I, 0);
-  const int sub = blockIdx.x % kSub, wt = (blockIdx.x / kSub) % geom.n_wt;
-  const int t = (blockIdx.x / kSub) / geom.n_wt, G = geom.G;
+  // CT = 1: the two blocks of one packed half (column tiles 2h and 2h + 1
+  // read the same 16-byte code vectors) are blocks b and b + 8, which run on
+  // one XCD (blocks go to XCD b % 8 in turn), so the second finds the codes
+  // in that XCD's L2 instead of fetching them again (the grid is a multiple
+  // of 16: H % 256 == 0)
+  int sub, wt, t;
+  if (CT == 1) {
+    const int xcd = blockIdx.x & 7, l = blockIdx.x >> 3;
+    const int m = ((l >> 1) << 3) | xcd;  // (token, wave tile, half)
+    sub = 2 * (m & 1) + (l & 1);
+    wt = (m >> 1) % geom.n_wt;
+    t = (m >> 1) / geom.n_wt;
+  } else {
+    sub = blockIdx.x % kSub;
+    wt = (blockIdx.x / kSub) % geom.n_wt;
+    t = (blockIdx.x / kSub) / geom.n_wt;
+  }
+  const int G = geom.G;
   const int ct0 = CT * sub;  // first column tile of the block
   const int half = ct0 >> 1, odd = ct0 & 1;
   const ExpandConsts xk = expand_consts();
@@ -551,7 +567,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
   if ((e = launch_gateup(gu.G, slots, gu.n_wt, a.T, s, a)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return e;
   if (a.T == 1)
-    hipLaunchKernelGGL(decode_down_kernel<1>, dim3(a.T * dn.n_wt * 4), dim3(kDecThreads), 0, s, a);
+    hipLaunchKernelGGL(decode_down_kernel<1>, dim3(a.T * dn.n_wt * 4), dim3(kDecThreads), 0, s, a);  // (a multiple of 16)
   else
     hipLaunchKernelGGL(decode_down_kernel<2>, dim3(a.T * dn.n_wt * 2), dim3(kDecThreads), 0, s, a);
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return e;

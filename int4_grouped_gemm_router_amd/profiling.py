@@ -15,8 +15,9 @@ Commands (run from the repository root):
         --copy-fetch DIR --copy-write DIR --kernel NAME --grid N --command ... --out FILE
       Mean FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of one kernel, scaled
       by the factors the copy dispatches give, as HBM bytes per launch. The
-      result records a digest of the kernel's sources; bench.py reports the
-      traffic only while the sources still match it.
+      result records a digest of the kernel's sources (--sources gemm or
+      decode); bench.py reports the gate/up traffic only while the sources
+      still match it.
 
   python3 -m int4_grouped_gemm_router_amd.profiling counters --dir DIR [--dir DIR ...] \
         --command ... --out FILE
@@ -38,8 +39,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 256 << 20
 
-# sources that define the grouped GEMM kernels' code
-GEMM_SOURCES = ["csrc/gemm.hip", "csrc/kernels.h", "csrc/device.h", "csrc/layout.h"]
+# sources that define the grouped GEMM kernels' code, and the decode kernels'
+GEMM_SOURCES = ["csrc/gemm.hip", "csrc/gemm_wide.hip", "csrc/kernels.h", "csrc/device.h", "csrc/layout.h"]
+DECODE_SOURCES = ["csrc/decode.hip", "csrc/topk.h", "csrc/kernels.h", "csrc/device.h", "csrc/layout.h"]
 
 
 def sources_digest(files=GEMM_SOURCES) -> str:
@@ -120,7 +122,7 @@ def traffic(a):
         "copy_bytes": COPY_BYTES, "copy_fetch_kib": fcopy, "copy_write_kib": wcopy,
         "fetch_scale": ff, "write_scale": wf,
         "hbm_bytes_per_launch": fkib * 1024 * ff + wkib * 1024 * wf,
-        "sources": GEMM_SOURCES, "sources_sha256": sources_digest(),
+        "sources": a.sources, "sources_sha256": sources_digest(a.sources),
         "commands": a.command,
     }
     with open(a.out, "w") as f:
@@ -198,11 +200,15 @@ def main(argv=None):
         t.add_argument("--" + n.replace("_", "-"), dest=n, required=True)
     t.add_argument("--grid", type=int, default=None)
     t.add_argument("--command", action="append", default=[])
+    t.add_argument("--sources", choices=["gemm", "decode"], default="gemm",
+                   help="source set whose digest the summary records")
     c = sub.add_parser("counters")
     c.add_argument("--dir", action="append", required=True)
     c.add_argument("--command", action="append", default=[])
     c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
+    if a.cmd == "traffic":
+        a.sources = GEMM_SOURCES if a.sources == "gemm" else DECODE_SOURCES
     if a.cmd == "copy":
         run_copy()
     elif a.cmd == "kernel-stats":
