@@ -257,8 +257,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(DecodeArgs a
   const int c16 = lane & 15, kb = lane >> 4;
   const int T = a.T, P = T * kK, H = a.H, I = a.I;
   const PackGeom geom = pack_geom(I, H, 1);
-  const int half0 = NH == 2 ? 0 : blockIdx.x & 1;  // first half of the block
-  const int tile = NH == 2 ? blockIdx.x : blockIdx.x >> 1;
+  // NH = 1: the two half blocks of a wave tile (they read the same
+  // scale/bias records) are blocks b and b + 8, which run on one XCD (blocks
+  // go to XCD b % 8 in turn), so the second finds the records in that XCD's
+  // L2; the grid is rounded up to a multiple of 16 and the extra blocks exit
+  int half0 = 0, tile = blockIdx.x;
+  if (NH == 1) {
+    const int xcd = blockIdx.x & 7, l = blockIdx.x >> 3;
+    half0 = l & 1;
+    tile = ((l >> 1) << 3) | xcd;
+    if (tile >= (P + 1) * geom.n_wt) return;
+  }
   // the shared expert's tiles first, then the unique routed experts in
   // order: blocks past the unique experts (which exit at once) come last
   const int sraw = tile / geom.n_wt, wt = tile % geom.n_wt;
@@ -548,7 +557,7 @@ hipError_t launch_gateup_nh(int G, dim3 grid, hipStream_t s, const DecodeArgs& a
 
 // Half-tile blocks at one token, whole wave tiles from two tokens on.
 hipError_t launch_gateup(int G, int slots, int n_wt, int T, hipStream_t s, const DecodeArgs& a) {
-  if (T == 1) return launch_gateup_nh<1>(G, dim3(slots * n_wt * 2), s, a);
+  if (T == 1) return launch_gateup_nh<1>(G, dim3((slots * n_wt * 2 + 15) / 16 * 16), s, a);
   return launch_gateup_nh<2>(G, dim3(slots * n_wt), s, a);
 }
 
