@@ -1,5 +1,5 @@
 // Grouped expert GEMMs for long chunks: int4 weights expanded once to bf16
-// per (expert, 256-column tile, 64-input group) and shared by up to 128 rows
+// per (expert, 512-column tile, 64-input group) and shared by up to 128 rows
 // of that expert (gfx950, bf16 matrix cores, fp32 accumulation).
 //
 // diariobitcoin.com, "Perplexity libera Lily, un motor de IA que supera a
@@ -10,20 +10,21 @@
 // in groups of 64 with a bf16 scale and bias, w = q * scale + bias.
 //
 // A work unit is one work item (up to 128 rows of one expert in
-// expert-sorted order, or 128 tokens of the shared expert) times a 256-column
-// tile of the output. A block of four waves takes one unit; wave w owns the
-// 64 columns of packed wave tile 4 nt + w for all of the item's rows (eight
-// 16-row subtiles, 128 fp32 accumulators per lane). Per 64-input group:
+// expert-sorted order, or 128 tokens of the shared expert) times a 512-column
+// tile of the output. A block of eight waves takes one unit; wave w owns the
+// 64 columns of packed wave tile 8 nt + w for all of the item's rows (up to
+// eight 16-row subtiles, 128 fp32 accumulators per lane). Per 64-input group:
 //   * the gathered activation rows (128 x 64 bf16 = 16 KB) are loaded by all
-//     256 threads into registers during the previous group's step, then
+//     512 threads into registers during the previous group's step, then
 //     written to a two-stage LDS buffer in the matrix-core A-operand order,
-//     and all four waves read them;
+//     and all eight waves read them;
 //   * each lane loads the packed codes of its own B-operand positions (the
 //     packed layout puts them there) and their scale/bias record about one
 //     and a half groups ahead, and expands them to bf16 w = q s + b in
-//     registers: the codes
-//     become exact fp16 values 1024 + q or 1024 + 16 q by one AND-OR each,
-//     one mixed-precision FMA per weight forms fp32 q s + b with a single
+//     registers: each pair of codes becomes the exact fp16 pair
+//     (1024 + q, 1024 + q') by a shift and one AND-OR (no shift for the
+//     lowest pair), one mixed-precision FMA per weight forms fp32 q s + b
+//     with a single
 //     rounding ((1024 + q) s + (b - 1024 s), the product exact), and one
 //     conversion rounds two weights to bf16 (nearest even);
 //   * the matrix cores accumulate x . w directly (v_mfma_f32_16x16x32_bf16).
