@@ -430,6 +430,43 @@ def test_other_family_sizes(torch_cuda, H, I, E):
         print(f"decode T={T} H={H} I={I} E={E}: {s}")
 
 
+# The wide GEMMs at the same family sizes (their automatic choice needs
+# thousands of tokens): 300 tokens forced wide, every token against the
+# oracle, reaching gate/up over 64 groups (H = 4096), 128 gate/up wave tiles
+# and a down K of 4096 (I = 4096, 64 groups per item), and the partial last
+# 512-column tile (I = 384 and 640: 12 and 20 wave tiles; H = 768).
+@pytest.mark.parametrize("H,I,E", [(1024, 384, 128), (4096, 256, 64), (768, 640, 192), (256, 4096, 64)])
+def test_other_family_sizes_wide(torch_cuda, H, I, E):
+    rng = np.random.default_rng(H + I + E + 1)
+    w = synth.make_weights(rng, H, I, E)
+    dw = B.DeviceWeights.from_logical(w)
+    d = B.dims(H, I, E, gemm=B.GEMM_WIDE)
+    x = synth.make_x(rng, 300, H)
+    y, logits, meta = _prefill(torch_cuda, dw, x, d=d)
+    idx, wsel = _route_of(meta, 300)
+    s = check_layer(x, w, y, logits, idx, wsel)
+    print(f"wide prefill H={H} I={I} E={E}: {s}")
+
+
+def test_gemm_auto_threshold(torch_cuda):
+    # the automatic choice takes the wide GEMMs from 32 pairs per expert on
+    # (8 T >= 32 E: T >= 1024 at E = 256): bit for bit the forced choice on
+    # each side of the threshold, and the two choices differ
+    _, w, dw = _layer("prefill_t512")
+    x = synth.make_x(np.random.default_rng(33), 1024, w.H)
+    auto = B.dims(w.H, w.I)
+    exact = B.dims(w.H, w.I, gemm=B.GEMM_EXACT)
+    wide = B.dims(w.H, w.I, gemm=B.GEMM_WIDE)
+    for T, same in ((1023, exact), (1024, wide)):
+        ya, _, _ = _prefill(torch_cuda, dw, x[:T], route=False, d=auto)
+        yf, _, _ = _prefill(torch_cuda, dw, x[:T], route=False, d=same)
+        other = wide if same is exact else exact
+        yo, _, _ = _prefill(torch_cuda, dw, x[:T], route=False, d=other)
+        assert np.array_equal(ya, yf), T
+        assert not np.array_equal(ya, yo), T
+        assert_y_close(synth.bf16_bits_to_f32(ya), synth.bf16_bits_to_f32(yo), f"T={T} exact vs wide")
+
+
 def test_prefill_graph_replay_matches_eager(torch_cuda):
     """The layer captured in a HIP graph and replayed (with eager work and
     synchronisations in between) gives exactly the eager output every time."""
