@@ -238,13 +238,40 @@ def run_decode(name, steps, warmup, copies):
     # shared experts' weights
     gemv_ms = float(kern_ms[0] + kern_ms[1] + kern_ms[2])
     ms_step = wall * 1e3 / steps
-    return dict(workload=name, T=T, steps=steps, ms_per_step=ms_step,
-                ms_per_step_eager=wall_eager * 1e3 / steps, graph_matches_eager=graph_ok,
-                unique_experts=U, kernels_us={k: float(v * 1e3) for k, v in zip(DECODE_KERNELS, kern_ms)},
-                gemv_bytes=gemv_bytes + router_bytes,
-                gemv_gbs=(gemv_bytes + router_bytes) / (gemv_ms / 1e3) / 1e9,
-                step_bytes=gemv_bytes + router_bytes,
-                end_to_end_gbs=(gemv_bytes + router_bytes) / (ms_step / 1e3) / 1e9)
+    res = dict(workload=name, T=T, steps=steps, ms_per_step=ms_step,
+               ms_per_step_eager=wall_eager * 1e3 / steps, graph_matches_eager=graph_ok,
+               unique_experts=U, kernels_us={k: float(v * 1e3) for k, v in zip(DECODE_KERNELS, kern_ms)},
+               gemv_bytes=gemv_bytes + router_bytes,
+               gemv_gbs=(gemv_bytes + router_bytes) / (gemv_ms / 1e3) / 1e9,
+               step_bytes=gemv_bytes + router_bytes,
+               end_to_end_gbs=(gemv_bytes + router_bytes) / (ms_step / 1e3) / 1e9)
+    # HBM roofline of the step's three kernels: algorithmic bytes over their
+    # summed event times; traffic = the committed FETCH_SIZE / WRITE_SIZE
+    # bytes of the three launches (null if missing or stale)
+    res["roofline"] = {"bound": "hbm", "achieved": res["gemv_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                       "frac": res["gemv_gbs"] / PEAK_HBM_GBS, "traffic": decode_traffic(name),
+                       "kernel": "+".join(DECODE_KERNELS), "per_step_bytes": res["gemv_bytes"],
+                       "mean_us": gemv_ms * 1e3}
+    return res
+
+
+def decode_traffic(workload):
+    """HBM bytes of one decode step (router, gate/up and down launches) from
+    the committed traffic summaries, or None when one is missing or was taken
+    from different decode sources."""
+    from int4_grouped_gemm_router_amd import profiling
+    total = 0.0
+    for k in ("router", "gateup", "down"):
+        f = os.path.join(ROOT, "profiles", f"traffic_decode_{k}_{workload}.json")
+        if not os.path.exists(f):
+            return None
+        with open(f) as fh:
+            t = json.load(fh)
+        if t.get("sources_sha256") != profiling.sources_digest(profiling.DECODE_SOURCES):
+            log(f"decode traffic summary {os.path.basename(f)} is stale")
+            return None
+        total += t["hbm_bytes_per_launch"]
+    return total
 
 
 def cpu_model():
