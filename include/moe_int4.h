@@ -68,7 +68,7 @@ extern "C" {
  *                   bias are applied per output and group in fp32 (weights
  *                   used exactly); suited to short chunks, where few rows
  *                   share an expert and the layer streams weights from HBM;
- *   MOE_GEMM_WIDE   work items of up to 128 rows of one expert; each weight
+ *   MOE_GEMM_WIDE   work items of up to 144 rows of one expert; each weight
  *                   is expanded once per item to bf16 w = q*scale + bias
  *                   (fp32 value rounded once to bf16) and the matrix cores
  *                   accumulate x.w in fp32; suited to long chunks, where many

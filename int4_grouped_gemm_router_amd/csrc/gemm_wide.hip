@@ -1,5 +1,5 @@
 // Grouped expert GEMMs for long chunks: int4 weights expanded once to bf16
-// per (expert, 512-column tile, 64-input group) and shared by up to 128 rows
+// per (expert, 512-column tile, 64-input group) and shared by up to 144 rows
 // of that expert (gfx950, bf16 matrix cores, fp32 accumulation).
 //
 // diariobitcoin.com, "Perplexity libera Lily, un motor de IA que supera a
@@ -9,12 +9,15 @@
 // section "Qwen3.6 combina tres cargas de trabajo": weights are affine 4-bit
 // in groups of 64 with a bf16 scale and bias, w = q * scale + bias.
 //
-// A work unit is one work item (up to 128 rows of one expert in
-// expert-sorted order, or 128 tokens of the shared expert) times a 512-column
+// A work unit is one work item (up to 144 rows of one expert in
+// expert-sorted order, or 144 tokens of the shared expert) times a 512-column
 // tile of the output. A block of eight waves takes one unit; wave w owns the
 // 64 columns of packed wave tile 8 nt + w for all of the item's rows (up to
-// eight 16-row subtiles, 128 fp32 accumulators per lane). Per 64-input group:
-//   * the gathered activation rows (128 x 64 bf16 = 16 KB) are loaded by all
+// nine 16-row subtiles, 144 fp32 accumulators per lane: 144 rows rather than
+// 128 so that an expert a little above 128 rows in a chunk, common when the
+// chunk averages 128 rows per expert, does not pay a second expansion of its
+// weights for a few rows). Per 64-input group:
+//   * the gathered activation rows (144 x 64 bf16 = 18 KB) are loaded by all
 //     512 threads into registers during the previous group's step, then
 //     written to a two-stage LDS buffer in the matrix-core A-operand order,
 //     and all eight waves read them;
@@ -47,19 +50,20 @@ constexpr int kWRows = kWideRows;       // rows per work item
 constexpr int kWSub = kWRows / 16;      // 16-row subtiles
 constexpr int kWWaves = 8;
 constexpr int kWThreads = kWWaves * 64;
-constexpr int kWChunks = kWRows * kGroup * 2 / 16 / kWThreads;  // 16-byte activation chunks per thread and group
 constexpr int kWSubPerChunk = kWThreads / 128;                   // subtiles one chunk index covers
-static_assert(kWChunks * kWSubPerChunk == kWSub, "activation staging covers every subtile");
+constexpr int kWChunks = (kWSub + kWSubPerChunk - 1) / kWSubPerChunk;  // 16-byte activation chunks per thread and group
+constexpr int kWStaged = kWChunks * kWSubPerChunk;                // subtiles the staging covers (>= kWSub)
+constexpr int kWTabRows = 16 * kWStaged;                          // rows of the row tables
 
 struct WideLds {
   union {
     // [stage][subtile][k half][lane]: the A fragments of one group
-    u32x4 a[2][kWSub][2][64];
+    u32x4 a[2][kWStaged][2][64];
     // epilogue: one 8 KB transpose buffer per wave
-    uint8_t tr[kWWaves][8192];
+    uint8_t tr[kWWaves][kWRows * 64];
   };
-  uint32_t rowoff[kWRows];  // byte offset of each row's activations from the unit's base
-  int outrow[kWRows];   // down: output row (pair index, or token of a shared row)
+  uint32_t rowoff[kWTabRows];  // byte offset of each row's activations from the unit's base
+  int outrow[kWTabRows];   // down: output row (pair index, or token of a shared row)
 };
 
 struct WideExpand {
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(GemmArgs a) {
   const uint32_t abytes = MODE == kGateUp ? (uint32_t)((int64_t)a.T * K * 2) : (uint32_t)(rows * K * 2);
   // row tables: byte offset of each row's activations from abase (rows past
   // the item repeat row 0) and, for down, the output row
-  if (tid < kWRows) {
+  if (tid < kWTabRows) {
     const int m = tid < rows ? tid : 0;
     int orow = 0;
     uint32_t aoff;
@@ -296,15 +300,17 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(GemmArgs a) {
     run(std::integral_constant<int, 4>{});
   else if (nsub <= 6)
     run(std::integral_constant<int, 6>{});
-  else
+  else if (nsub <= 8)
     run(std::integral_constant<int, 8>{});
+  else
+    run(std::integral_constant<int, kWSub>{});
 
   // ---- epilogue: per-wave transpose through this wave's 8 KB of LDS (the
   // last step's barrier ended every read of the activation stages)
   uint8_t* tb = &L.tr[wave][0];
   if (!wt_active) return;
   if (MODE == kGateUp) {
-    // h = bf16(silu(gate) * up): 128 rows x 32 intermediate columns
+    // h = bf16(silu(gate) * up): up to 144 rows x 32 intermediate columns
     const int I = a.N;
     uint16_t* trb = reinterpret_cast<uint16_t*>(tb);
 #pragma unroll
@@ -333,10 +339,11 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(GemmArgs a) {
     // 32 rows x 64 columns of fp32 per round
     float* trf = reinterpret_cast<float*>(tb);
 #pragma unroll
-    for (int mp = 0; mp < kWSub / 2; ++mp) {
+    for (int mp = 0; mp < (kWSub + 1) / 2; ++mp) {
       if (2 * mp < nsub) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
+          if (2 * mp + h2 < kWSub)
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct)
 #pragma unroll

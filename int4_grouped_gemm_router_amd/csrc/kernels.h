@@ -12,7 +12,7 @@ namespace moe {
 
 constexpr int kChunkPairs = 1024;  // (token, slot) pairs per scatter block
 constexpr int kItemRows = 32;      // most rows of one expert per GEMM work item (one routing block)
-constexpr int kWideRows = 128;     // rows per work item of the wide GEMMs
+constexpr int kWideRows = 144;     // rows per work item of the wide GEMMs
 constexpr int kMaxGroups = 64;     // K / 64 upper bound of the expert GEMMs
 constexpr int kDecodeMaxT = 4;
 constexpr int kMaxSplits = 8;      // router K splits summed by the top-k kernel

@@ -154,7 +154,7 @@ def test_prefill_unfused_matches_oracle(torch_cuda):
 
 
 def test_prefill_skew_t2048_all_tokens(torch_cuda):
-    # the Zipf-skewed workload (automatic choice: the wide 128-row GEMMs),
+    # the Zipf-skewed workload (automatic choice: the wide 144-row GEMMs),
     # every token against the oracle
     wl, w, dw = _layer("skew_t2048")
     _, _, x = synth.generate("skew_t2048", with_x=True)
@@ -200,7 +200,7 @@ def test_prefill_long_chunked_all_tokens(torch_cuda):
 
 @pytest.mark.parametrize("T", [1, 5, 100, 300])
 def test_prefill_wide_tiny_all_tokens(torch_cuda, T):
-    # the wide GEMMs (items of up to 128 rows, bf16 weights expanded once per
+    # the wide GEMMs (items of up to 144 rows, bf16 weights expanded once per
     # item) forced on the tiny layer: one gate/up and two down column tiles,
     # 8 and 2 groups, ragged items and shared items
     wl, w, dw = _layer("tiny_t32")
@@ -214,7 +214,7 @@ def test_prefill_wide_tiny_all_tokens(torch_cuda, T):
 
 
 def test_prefill_wide_forced_heavy_routing(torch_cuda):
-    # twelve experts take nearly every pair: items of 128 rows plus ragged
+    # twelve experts take nearly every pair: items of 144 rows plus ragged
     # tails, 244 empty experts; wide and exact GEMMs both against the oracle
     import copy
     _, w, _ = _layer("tiny_t32")
