@@ -706,12 +706,10 @@ __global__ void test_dequant_kernel(const uint8_t* ebase, int N, int K, int pair
   }
 }
 
-namespace {
-
-// Persistent grid: one block per compute unit (a multiple of 8 for the XCD
+// Persistent grids: one block per compute unit (a multiple of 8 for the XCD
 // mapping). The per-device count is cached; concurrent first calls may both
 // query it and store the same value (relaxed atomics, no lock needed).
-int persistent_blocks() {
+int compute_units() {
   static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -727,6 +725,8 @@ int persistent_blocks() {
   return v;
 }
 
+namespace {
+
 template <int MODE>
 hipError_t launch_mode(const GemmArgs& a, hipStream_t s, int grid_blocks) {
   if (a.bf16_weights) {
@@ -734,13 +734,13 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s, int grid_blocks) {
     if (G % 2) return hipErrorInvalidValue;
     const int exact = (grid_blocks + 7) / 8 * 8;
     hipLaunchKernelGGL((gemm_ring_kernel<MODE, true>),
-                       dim3(grid_blocks > 0 ? exact : kRBlocksPerCU * persistent_blocks()),
+                       dim3(grid_blocks > 0 ? exact : kRBlocksPerCU * compute_units()),
                        dim3(kRThreads), 0, s, a);
     return hipGetLastError();
   }
   const int G = a.K / kGroup;
   if (G < 2 || G > kMaxGroups) return hipErrorInvalidValue;
-  const int cus = persistent_blocks();
+  const int cus = compute_units();
   const int exact = (grid_blocks + 7) / 8 * 8;
   if (G % kRS == 0) {
     const dim3 grid(grid_blocks > 0 ? exact : kRBlocksPerCU * cus), block(kRThreads);

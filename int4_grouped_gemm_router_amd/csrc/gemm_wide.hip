@@ -121,12 +121,21 @@ __device__ inline u32x4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
 
 }  // namespace
 
-// Grid: 8 * n_tiles * ceil(max_slots / 8) blocks of 512 threads. Block b runs
-// on XCD b & 7; with l = b >> 3, it takes slot 8 (l / n_tiles) + (b & 7) and
-// column tile l % n_tiles, so the column tiles of one item run on one XCD
+// Grid: 8 * n_tiles * ceil(max_slots / 8) blocks of 512 threads. Block b
+// runs on XCD b & 7; with l = b >> 3, it takes slot 8 (l / n_tiles) + (b & 7)
+// and column tile l % n_tiles, so the column tiles of one item run on one XCD
 // (their activation rows shared in its L2). Blocks are handed out in index
 // order, so the work list's longest-first order makes the launch a greedy
 // longest-first schedule per XCD. Slots past the work list exit at once.
+//
+// Column halves (gate/up): one block per compute unit runs at a time, so V
+// units take about V / cus rounds, and a last round of rem = V mod cus units
+// leaves the other compute units idle for a whole unit time. When
+// rem <= cus / 2, the last rem units in dispatch order run as two
+// 256-column halves instead (half 0 in the unit's own block, half 1 in one
+// of the blocks past the work list): the last round then takes about half a
+// unit time. A half computes each of its outputs by the same operations in
+// the same order as the whole unit, so results do not depend on the split.
 template <int MODE>
 __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(GemmArgs a) {
   __shared__ WideLds L;
@@ -136,10 +145,43 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(GemmArgs a) {
   const int K = a.K, G = K / kGroup;
   const PackGeom geom = pack_geom(a.N, K, a.paired);
   const int n_tiles = (geom.n_wt + kWWaves - 1) / kWWaves;
-  const int xcd = blockIdx.x & 7, l = blockIdx.x >> 3;
-  const int slot = 8 * (l / n_tiles) + xcd, nt = l % n_tiles;
   const int ni = *a.num_items;
-  if (slot >= ni + a.shared_slots) return;
+  const int n_slots = ni + a.shared_slots;
+  const int n_units = n_slots * n_tiles;
+  // dispatch rank of unit block (slot 8 r + x, tile t): rows of 8 slots,
+  // tile-major within a row; the last row holds n_slots & 7 slots
+  const int full_rows = n_slots >> 3, last_row = n_slots & 7;
+  const int full_units = 8 * n_tiles * full_rows;
+  // blocks from first_free on have no unit (the grid is sized for the most
+  // work items); the first of them take the second column halves
+  const int first_free = 8 * n_tiles * (full_rows + (last_row > 0 ? 1 : 0));
+  const int rem = n_units % a.cus;
+  int split = MODE == kGateUp && rem <= a.cus / 2 ? rem : 0;  // units run as column halves
+  split = min(split, max(0, (int)gridDim.x - first_free));
+  int slot, nt, hsel = -1;  // hsel: -1 the whole unit, 0 / 1 its column half
+  if ((int)blockIdx.x < first_free) {
+    const int x = blockIdx.x & 7, l = blockIdx.x >> 3;
+    const int r = l / n_tiles, t = l % n_tiles;
+    slot = 8 * r + x;
+    nt = t;
+    if (slot >= n_slots) return;
+    const int rank = r < full_rows ? 8 * n_tiles * r + 8 * t + x : full_units + last_row * t + x;
+    if (rank >= n_units - split) hsel = 0;
+  } else {
+    const int i = (int)blockIdx.x - first_free;
+    if (i >= split) return;
+    const int v = n_units - split + i;  // rank of the unit whose half 1 this is
+    if (v < full_units) {
+      const int r = v / (8 * n_tiles), q = v % (8 * n_tiles);
+      nt = q >> 3;
+      slot = 8 * r + (q & 7);
+    } else {
+      const int q = v - full_units;  // last_row > 0 here
+      nt = q / last_row;
+      slot = 8 * full_rows + q % last_row;
+    }
+    hsel = 1;
+  }
 
   // slots: the shared expert's items (full ones first), then the work list
   // (full items, then partial ones, larger first)
@@ -189,9 +231,12 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(GemmArgs a) {
   for (int i = 0; i < kWChunks; ++i) aoffs[i] = L.rowoff[16 * (kWSubPerChunk * i + spar) + c16] + 16 * sj;
   const int sks = sj >> 2, slane = (sj & 3) * 16 + c16;
 
-  // this lane's codes and scale/bias records (wave tile 8 nt + wave; the
-  // waves past the matrix's last wave tile repeat it and store nothing)
-  const int wt_raw = nt * kWWaves + wave;
+  // this lane's codes and scale/bias records: a whole unit's wave w takes
+  // wave tile 8 nt + w (16-column tiles 0-3); in a column half, wave w takes
+  // tiles 2 (w & 1) and 2 (w & 1) + 1 of wave tile 8 nt + 4 hsel + w / 2. The
+  // waves past the matrix's last wave tile repeat it and store nothing.
+  const int wt_raw = hsel < 0 ? nt * kWWaves + wave : nt * kWWaves + 4 * hsel + (wave >> 1);
+  const int ch = hsel < 0 ? 0 : (wave & 1);  // which pair of 16-column tiles (halves)
   const bool wt_active = wt_raw < geom.n_wt;
   const int wt = wt_active ? wt_raw : geom.n_wt - 1;
   const uint8_t* eb = routed ? a.blob + (int64_t)expert * a.expert_bytes : a.shared_blob;
@@ -210,10 +255,17 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(GemmArgs a) {
     for (int i = 0; i < kWChunks; ++i)
       if (kWSubPerChunk * i < ns) dst[i] = bload(ares, aoffs[i], (uint32_t)g * (kGroup * 2));
   };
-  auto load_w = [&](int g, u32x4 (&c)[2], u32x4& sv) {
+  // CT 16-column tiles per wave: 4 (whole units: both 16-byte halves of the
+  // lane's codes) or 2 (column halves: the half holding tiles 2 ch, 2 ch + 1)
+  auto load_w = [&](int g, u32x4 (&c)[2], u32x4& sv, auto CT_) {
+    constexpr int CT = decltype(CT_)::value;
     g = min(g, G - 1);
-    c[0] = bload(wres, lane * 16, nbase + (uint32_t)g * kNibBytes);
-    c[1] = bload(wres, lane * 16, nbase + (uint32_t)g * kNibBytes + 1024);
+    if constexpr (CT == 4) {
+      c[0] = bload(wres, lane * 16, nbase + (uint32_t)g * kNibBytes);
+      c[1] = bload(wres, lane * 16, nbase + (uint32_t)g * kNibBytes + 1024);
+    } else {
+      c[0] = bload(wres, lane * 16, nbase + (uint32_t)g * kNibBytes + 1024 * ch);
+    }
     sv = bload(wres, c16 * 16, sbase + (uint32_t)g * kSbBytes);
   };
   auto store_act = [&](int st, const u32x4 (&src)[kWChunks], int ns) {
@@ -241,13 +293,14 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(GemmArgs a) {
   // of group g + 2 are loaded once step g has expanded group g's. S = g % 2
   // (register slot, LDS stage) is a compile-time constant so the rings stay
   // in registers.
-  auto run = [&](auto NS_) {
+  auto run = [&](auto NS_, auto CT_) {
     constexpr int NS = decltype(NS_)::value;
+    constexpr int CT = decltype(CT_)::value;
     auto frag = [&](int S, int f) -> u32x4 { return L.a[S][f % NS][f / NS][lane]; };
     // prologue: codes of groups 0 and 1 in flight, group 0's activations in LDS
     load_act(0, ax, NS);
-    load_w(0, cw[0], sbv[0]);
-    load_w(1, cw[1], sbv[1]);
+    load_w(0, cw[0], sbv[0], CT_);
+    load_w(1, cw[1], sbv[1], CT_);
     store_act(0, ax, NS);
     __syncthreads();
     auto step = [&](int g, auto S_) {
@@ -255,21 +308,27 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(GemmArgs a) {
       load_act(g + 1, ax, NS);  // to LDS at the end of this step
       u32x4 af[2];
       af[0] = frag(S, 0);
-      ColAffine ca[4];
+      ColAffine ca[CT];
       {
         const u32x4 sb = sbv[S];
-        const float sc[4] = {bf16lo(sb.x), bf16hi(sb.x), bf16lo(sb.y), bf16hi(sb.y)};
-        const float bi[4] = {bf16lo(sb.z), bf16hi(sb.z), bf16lo(sb.w), bf16hi(sb.w)};
+        if constexpr (CT == 4) {
+          const float sc[4] = {bf16lo(sb.x), bf16hi(sb.x), bf16lo(sb.y), bf16hi(sb.y)};
+          const float bi[4] = {bf16lo(sb.z), bf16hi(sb.z), bf16lo(sb.w), bf16hi(sb.w)};
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) ca[ct] = col_affine(sc[ct], bi[ct]);
+          for (int ct = 0; ct < 4; ++ct) ca[ct] = col_affine(sc[ct], bi[ct]);
+        } else {
+          const uint32_t sp = ch ? sb.y : sb.x, bp = ch ? sb.w : sb.z;
+          ca[0] = col_affine(bf16lo(sp), bf16lo(bp));
+          ca[1] = col_affine(bf16hi(sp), bf16hi(bp));
+        }
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        u32x4 bw[4];  // this k half's B operands
+        u32x4 bw[CT];  // this k half's B operands
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) bw[ct] = expand_bf16(word(cw[S], 2 * ct + ks), ca[ct], xk);
+        for (int ct = 0; ct < CT; ++ct) bw[ct] = expand_bf16(word(cw[S], 2 * ct + ks), ca[ct], xk);
         // every word of slot S is expanded: its registers take group g + 2
-        if (ks == 1) load_w(g + 2, cw[S], sbv[S]);
+        if (ks == 1) load_w(g + 2, cw[S], sbv[S], CT_);
 #pragma unroll
         for (int ms = 0; ms < NS; ++ms) {
           const int f = ks * NS + ms;
@@ -277,7 +336,7 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(GemmArgs a) {
           __builtin_amdgcn_sched_barrier(0);
           const u32x4 av = af[f % 2];
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct) acc[ms][ct] = mfma16(av, bw[ct], acc[ms][ct]);
+          for (int ct = 0; ct < CT; ++ct) acc[ms][ct] = mfma16(av, bw[ct], acc[ms][ct]);
         }
       }
       store_act(1 - S, ax, NS);  // group g + 1
@@ -292,51 +351,72 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(GemmArgs a) {
       step(g + 1, I1{});
     }
   };
-  if (nsub <= 1)
-    run(std::integral_constant<int, 1>{});
-  else if (nsub <= 2)
-    run(std::integral_constant<int, 2>{});
-  else if (nsub <= 4)
-    run(std::integral_constant<int, 4>{});
-  else if (nsub <= 6)
-    run(std::integral_constant<int, 6>{});
-  else if (nsub <= 8)
-    run(std::integral_constant<int, 8>{});
-  else
-    run(std::integral_constant<int, kWSub>{});
+  auto run_ns = [&](auto CT_) {
+    if (nsub <= 1)
+      run(std::integral_constant<int, 1>{}, CT_);
+    else if (nsub <= 2)
+      run(std::integral_constant<int, 2>{}, CT_);
+    else if (nsub <= 4)
+      run(std::integral_constant<int, 4>{}, CT_);
+    else if (nsub <= 6)
+      run(std::integral_constant<int, 6>{}, CT_);
+    else if (nsub <= 8)
+      run(std::integral_constant<int, 8>{}, CT_);
+    else
+      run(std::integral_constant<int, kWSub>{}, CT_);
+  };
+  if constexpr (MODE == kGateUp) {
+    if (hsel >= 0) {
+      run_ns(std::integral_constant<int, 2>{});
+    } else {
+      run_ns(std::integral_constant<int, 4>{});
+    }
+  } else {
+    run_ns(std::integral_constant<int, 4>{});
+  }
 
-  // ---- epilogue: per-wave transpose through this wave's 8 KB of LDS (the
+  // ---- epilogue: per-wave transpose through this wave's 9 KB of LDS (the
   // last step's barrier ended every read of the activation stages)
   uint8_t* tb = &L.tr[wave][0];
   if (!wt_active) return;
   if (MODE == kGateUp) {
-    // h = bf16(silu(gate) * up): up to 144 rows x 32 intermediate columns
+    // h = bf16(silu(gate) * up), gate/up in 16-column tile pairs (2 j, 2 j + 1):
+    // up to 144 rows x CW intermediate columns (CW = 32 whole, 16 in a half)
     const int I = a.N;
     uint16_t* trb = reinterpret_cast<uint16_t*>(tb);
+    auto store_h = [&](auto CW_) {
+      constexpr int CW = decltype(CW_)::value;
 #pragma unroll
-    for (int ms = 0; ms < kWSub; ++ms) {
-      if (ms < nsub) {
+      for (int ms = 0; ms < kWSub; ++ms) {
+        if (ms < nsub) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < CW / 16; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            trb[(16 * ms + 4 * kb + i) * 32 + 16 * j + c16] =
-                f2bf(silu(acc[ms][2 * j][i]) * acc[ms][2 * j + 1][i]);
+            for (int i = 0; i < 4; ++i)
+              trb[(16 * ms + 4 * kb + i) * CW + 16 * j + c16] =
+                  f2bf(silu(acc[ms][2 * j][i]) * acc[ms][2 * j + 1][i]);
+        }
       }
-    }
-    // (a wave's LDS accesses execute in order: no wait between its writes
-    // and its reads of the other lanes' values)
-    wide_fence();
+      // (a wave's LDS accesses execute in order: no wait between its writes
+      // and its reads of the other lanes' values)
+      wide_fence();
+      constexpr int kChunks = CW / 8;  // 16-byte pieces per row
+      const int col0 = 32 * wt + 16 * ch;
 #pragma unroll
-    for (int q = 0; q < kWRows * 4 / 64; ++q) {
-      const int c = lane + 64 * q, r = c >> 2, ch = c & 3;
-      if (r < rows) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(trb + r * 32 + 8 * ch);
-        *reinterpret_cast<u32x4*>(a.h_out + (int64_t)(row0 + r) * I + 32 * wt + 8 * ch) = v;
+      for (int q = 0; q < (kWRows * kChunks + 63) / 64; ++q) {
+        const int c = lane + 64 * q, r = c / kChunks, pc = c % kChunks;
+        if (r < rows) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(trb + r * CW + 8 * pc);
+          *reinterpret_cast<u32x4*>(a.h_out + (int64_t)(row0 + r) * I + col0 + 8 * pc) = v;
+        }
       }
-    }
+    };
+    if (hsel < 0)
+      store_h(std::integral_constant<int, 32>{});
+    else
+      store_h(std::integral_constant<int, 16>{});
   } else {
-    // 32 rows x 64 columns of fp32 per round
+    // 32 rows x 64 columns of fp32 per round (down has no column halves)
     float* trf = reinterpret_cast<float*>(tb);
 #pragma unroll
     for (int mp = 0; mp < (kWSub + 1) / 2; ++mp) {
@@ -373,9 +453,11 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(GemmArgs a) {
   }
 }
 
-hipError_t launch_gemm_wide(GemmMode mode, const GemmArgs& a, int max_slots, hipStream_t s) {
+hipError_t launch_gemm_wide(GemmMode mode, const GemmArgs& a_in, int max_slots, hipStream_t s) {
+  GemmArgs a = a_in;
   const PackGeom geom = pack_geom(a.N, a.K, a.paired);
   if (a.K % (2 * kGroup) || max_slots <= 0) return hipErrorInvalidValue;
+  a.cus = compute_units();
   const int n_tiles = (geom.n_wt + kWWaves - 1) / kWWaves;
   const int64_t blocks = 8LL * n_tiles * ((max_slots + 7) / 8);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;

@@ -63,7 +63,12 @@ struct GemmArgs {
   uint16_t* h_out;           // gate/up: h [(k+1)T][N] bf16
   uint16_t* partial_r;       // down, routed rows: [T*k][N] bf16 at pair p = t*k + j
   float* partial_s;          // down, shared-expert rows: [T][N] fp32
+  int cus;                   // wide GEMMs: compute units (set by the launcher)
 };
+
+// Compute units of the current device, rounded down to a multiple of 8 (the
+// XCD count); cached per device.
+int compute_units();
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* planes, float* partial, int T, int H,
                          int E, int splits, int* zero_buf, int zero_count, hipStream_t s);
