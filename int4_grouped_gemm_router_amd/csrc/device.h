@@ -74,7 +74,11 @@ __device__ inline void split_hi_lo(float v, uint16_t& hi, uint16_t& lo) {
   lo = (uint16_t)(__float_as_uint(r) >> 16);
 }
 
-__device__ inline float silu(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z) with the hardware exponential and reciprocal
+// (about one ulp each in fp32; every use rounds the result to bf16). An IEEE
+// division here cost about four times as many instructions, which made it
+// the largest part of the gate/up epilogue.
+__device__ inline float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Barrier for LDS hand-off only: waits for this wave's LDS operations, not
 // for its outstanding global loads (a plain __syncthreads would drain them).
