@@ -401,14 +401,21 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(GemmArgs a) {
       // and its reads of the other lanes' values)
       wide_fence();
       constexpr int kChunks = CW / 8;  // 16-byte pieces per row
+      constexpr int kQ = (kWRows * kChunks + 63) / 64;
       const int col0 = 32 * wt + 16 * ch;
+      // all of the lane's reads first, then the stores (one LDS wait, not
+      // one per store); rows past the item read this wave's own buffer
+      // (kWRows rows) and are not stored
+      u32x4 v[kQ];
 #pragma unroll
-      for (int q = 0; q < (kWRows * kChunks + 63) / 64; ++q) {
+      for (int q = 0; q < kQ; ++q) {
+        const int c = lane + 64 * q, r = min(c / kChunks, kWRows - 1), pc = c % kChunks;
+        v[q] = *reinterpret_cast<const u32x4*>(trb + r * CW + 8 * pc);
+      }
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
         const int c = lane + 64 * q, r = c / kChunks, pc = c % kChunks;
-        if (r < rows) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(trb + r * CW + 8 * pc);
-          *reinterpret_cast<u32x4*>(a.h_out + (int64_t)(row0 + r) * I + col0 + 8 * pc) = v;
-        }
+        if (r < rows) *reinterpret_cast<u32x4*>(a.h_out + (int64_t)(row0 + r) * I + col0 + 8 * pc) = v[q];
       }
     };
     if (hsel < 0)
@@ -429,23 +436,32 @@ __global__ __launch_bounds__(kWThreads, 1) void gemm_wide_kernel(GemmArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) trf[(16 * h2 + 4 * kb + i) * 64 + 16 * ct + c16] = acc[2 * mp + h2][ct][i];
         wide_fence();
+        // the round's eight values and output rows read first (one LDS wait,
+        // not one per store; the output-row table covers every row read)
+        f32x4 v[8];
+        int orow[8];
+        const int col = 64 * wt + 4 * (lane & 15);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const int c = lane + 64 * q, r = c >> 4, c4 = c & 15;
-          const int row = 32 * mp + r;
-          const f32x4 v = *reinterpret_cast<const f32x4*>(trf + r * 64 + 4 * c4);
-          if (row < rows) {
-            const int orow = L.outrow[row];
-            const int col = 64 * wt + 4 * c4;
-            if (routed) {
+          const int r = (lane >> 4) + 4 * q;
+          v[q] = *reinterpret_cast<const f32x4*>(trf + r * 64 + 4 * (lane & 15));
+          orow[q] = L.outrow[32 * mp + r];
+        }
+        if (routed) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            if (32 * mp + (lane >> 4) + 4 * q < rows) {
               u32x2 o;
-              o.x = pack_bf16x2(v.x, v.y);
-              o.y = pack_bf16x2(v.z, v.w);
-              *reinterpret_cast<u32x2*>(a.partial_r + (int64_t)orow * a.N + col) = o;
-            } else {
-              *reinterpret_cast<f32x4*>(a.partial_s + (int64_t)orow * a.N + col) = v;
+              o.x = pack_bf16x2(v[q].x, v[q].y);
+              o.y = pack_bf16x2(v[q].z, v[q].w);
+              *reinterpret_cast<u32x2*>(a.partial_r + (int64_t)orow[q] * a.N + col) = o;
             }
           }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (32 * mp + (lane >> 4) + 4 * q < rows)
+              *reinterpret_cast<f32x4*>(a.partial_s + (int64_t)orow[q] * a.N + col) = v[q];
         }
         wide_fence();
       }
