@@ -20,7 +20,9 @@ Prints ONE JSON line on stdout (progress goes to stderr):
                 on the library's stream around every launch in the timed region
                 (plus that rate over the measured ceiling below)
   ceilings      measured on this device in the same run: streaming HBM read
-                GB/s over a 2 GiB buffer and the bf16 MFMA loop's TFLOP/s
+                GB/s over a 2 GiB buffer and the bf16 MFMA loop's TFLOP/s on
+                random and on nearly constant operands, each with the shader
+                clock it sustained (the fractions use the random-operand rate)
   cpu_baseline  the CPU oracle timed on this host on the same workload
   roofline_mfma the matrix-core roofline (gate/up and down kernels, and the
                 whole layer's expert flops) of the two long-chunk workloads
@@ -306,14 +308,19 @@ def cpu_baseline(w, x, min_seconds=10.0):
             f"{dt:.1f} s wall"}
 
 
-def measure_ceilings(read_bytes=2 << 30, mfma_iters=4000, reps=5):
+def measure_ceilings(read_bytes=2 << 30, mfma_iters=1000, reps=5):
     """Achievable HBM read bandwidth and bf16 MFMA rate on this device, from the
     library's measurement kernels (a streaming read of a buffer 8x the 256 MB
-    last-level cache; independent 16x16x32 bf16 MFMA chains), best of `reps`."""
+    last-level cache; independent 16x16x32 bf16 MFMA chains), best of `reps`.
+    The MFMA loop runs twice: on random operands (what the layer's matrix
+    cores see, the ceiling the fractions are stated against) and on nearly
+    constant ones; each run also reports the shader clock it sustained
+    (s_memtime ticks over s_memrealtime's 100 MHz, summed over the blocks)."""
     import torch
     from int4_grouped_gemm_router_amd import binding as B
     buf = torch.empty(read_bytes, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(2 * B.CEILING_MFMA_BLOCKS, dtype=torch.int64, device="cuda")
 
     def best(fn):
         fn()
@@ -328,16 +335,21 @@ def measure_ceilings(read_bytes=2 << 30, mfma_iters=4000, reps=5):
         return min(ts)
 
     t_read = best(lambda: B.moe_ceiling_read(buf, sink))
-    flops = [0.0]
+    out = {"hbm_read_gbs": read_bytes / t_read / 1e9, "read_bytes": read_bytes}
+    for random, key in ((True, "mfma_bf16"), (False, "mfma_bf16_constant_operands")):
+        flops = [0.0]
 
-    def mfma():
-        flops[0] = B.moe_ceiling_mfma(mfma_iters, sink)
+        def mfma():
+            flops[0] = B.moe_ceiling_mfma(mfma_iters, sink, random=random, clocks=clocks)
 
-    t_mfma = best(mfma)
+        t = best(mfma)
+        out[key + "_tflops"] = flops[0] / t / 1e12
+        out[key + "_clock_mhz"] = B.ceiling_clock_mhz(clocks)
+    out["mfma_flops"] = flops[0]
+    out["method"] = ("moe_ceiling_read / moe_ceiling_mfma, best of %d event-timed launches; "
+                     "mfma_bf16 on random operands" % reps)
     del buf
-    return {"hbm_read_gbs": read_bytes / t_read / 1e9, "read_bytes": read_bytes,
-            "mfma_bf16_tflops": flops[0] / t_mfma / 1e12, "mfma_flops": flops[0],
-            "method": "moe_ceiling_read / moe_ceiling_mfma, best of %d event-timed launches" % reps}
+    return out
 
 
 def measured_traffic(workload):

@@ -96,7 +96,7 @@ def lib():
         L.moe_decode_layer_noalloc.argtypes = [P(MoeDims), P(MoeLayerWeights), _vp, _vp, _i32, _vp,
                                                P(MoeRouteOut), _vp]
         L.moe_ceiling_read.argtypes = [_vp, _sz, _vp, _vp]
-        L.moe_ceiling_mfma.argtypes = [_i32, _vp, P(ctypes.c_double), _vp]
+        L.moe_ceiling_mfma.argtypes = [_i32, _i32, _vp, _vp, P(ctypes.c_double), _vp]
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
         L.moe_test_dequant.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp]
@@ -374,12 +374,27 @@ def moe_ceiling_read(buf, sink, stream=None):
                                   _stream(stream)), "moe_ceiling_read")
 
 
-def moe_ceiling_mfma(iters: int, sink, stream=None) -> float:
-    """Enqueue the bf16 matrix-core loop; returns the launch's flop count."""
+CEILING_MFMA_BLOCKS = 1024  # blocks of the matrix-core loop (two clock values each)
+
+
+def moe_ceiling_mfma(iters: int, sink, random: bool = True, clocks=None, stream=None) -> float:
+    """Enqueue the bf16 matrix-core loop (random or nearly constant operands);
+    `clocks`, if given, is an int64 device tensor of 2 * CEILING_MFMA_BLOCKS
+    values that receives each block's real-time and shader-clock ticks.
+    Returns the launch's flop count."""
+    if clocks is not None and clocks.numel() * clocks.element_size() < 16 * CEILING_MFMA_BLOCKS:
+        raise ValueError("moe_ceiling_mfma: clocks needs 2 * CEILING_MFMA_BLOCKS int64 values")
     flops = ctypes.c_double(0.0)
-    _check(lib().moe_ceiling_mfma(iters, _ptr(sink), ctypes.byref(flops), _stream(stream)),
-           "moe_ceiling_mfma")
+    _check(lib().moe_ceiling_mfma(iters, int(random), _ptr(sink), _ptr(clocks), ctypes.byref(flops),
+                                  _stream(stream)), "moe_ceiling_mfma")
     return flops.value
+
+
+def ceiling_clock_mhz(clocks) -> float:
+    """Mean shader clock of the last moe_ceiling_mfma launch that wrote `clocks`
+    (shader-clock ticks over 100 MHz real-time ticks, summed over the blocks)."""
+    c = clocks.view(-1, 2).cpu().double()
+    return float(c[:, 1].sum() / c[:, 0].sum() * 100.0)
 
 
 def moe_test_dequant(blob, count, N, K, paired, expert, out, stream=None):

@@ -37,23 +37,55 @@ __global__ __launch_bounds__(kCeilThreads) void ceiling_read_kernel(const u32x4*
   if (x == kNever) sink[0] = x;
 }
 
-// Each wave runs kMfmaChains independent chains of 16x16x32 bf16 MFMAs on
-// register operands derived from the lane index.
-__global__ __launch_bounds__(kCeilThreads) void ceiling_mfma_kernel(int iters, float* sink) {
-  const uint32_t l = threadIdx.x;
-  const u32x4 a = {0x3F80u | (l << 16), 0x3F81u, 0x3F82u ^ l, 0x3F83u};
-  const u32x4 b = {0x3F84u, 0x3F85u | (l << 16), 0x3F86u, 0x3F87u ^ l};
+// Each wave runs kMfmaChains independent chains of 16x16x32 bf16 MFMAs.
+// Operands: with `random`, four A and four B fragments per lane hold random
+// bf16 values of magnitude in [0.5, 1) and random sign (a hash of the lane's
+// global index), and consecutive operations take different ones, so the
+// matrix cores switch as they do on layer data; otherwise the operands are
+// nearly constant. The device draws more power in the first case and
+// sustains a lower shader clock. If `clocks` is given, thread 0 of each block
+// writes the block's real-time ticks (s_memrealtime, 100 MHz) and shader
+// clock ticks (s_memtime) over its loop, from which the clock follows.
+__device__ inline uint32_t ceil_hash(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x85EBCA6Bu;
+  x ^= x >> 13;
+  x *= 0xC2B2AE35u;
+  return x ^ (x >> 16);
+}
+
+__global__ __launch_bounds__(kCeilThreads) void ceiling_mfma_kernel(int iters, int random, float* sink,
+                                                                    unsigned long long* clocks) {
+  const uint32_t l = threadIdx.x, g = blockIdx.x * kCeilThreads + l;
+  u32x4 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t ra = (ceil_hash(g * 32u + 4u * i + e) & 0x807F807Fu) | 0x3F003F00u;
+      const uint32_t rb = (ceil_hash(g * 32u + 16u + 4u * i + e) & 0x807F807Fu) | 0x3F003F00u;
+      a[i][e] = random ? ra : (e == 0 ? (0x3F80u | (l << 16)) : 0x3F813F81u);
+      b[i][e] = random ? rb : (e == 1 ? (0x3F85u | (l << 16)) : 0x3F843F84u);
+    }
   f32x4 acc[kMfmaChains];
 #pragma unroll
   for (int c = 0; c < kMfmaChains; ++c) acc[c] = f32x4{(float)c, 0.f, 0.f, 0.f};
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime(), c0 = __builtin_amdgcn_s_memtime();
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int c = 0; c < kMfmaChains; ++c) acc[c] = mfma16(a, b, acc[c]);
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int c = 0; c < kMfmaChains; ++c) acc[c] = mfma16(a[c % 4], b[(c / 4 + j) % 4], acc[c]);
   }
+  const unsigned long long t1 = __builtin_amdgcn_s_memrealtime(), c1 = __builtin_amdgcn_s_memtime();
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < kMfmaChains; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
   if (__float_as_uint(s) == kNever) sink[0] = s;
+  if (clocks && l == 0) {
+    clocks[2 * blockIdx.x] = t1 - t0;
+    clocks[2 * blockIdx.x + 1] = c1 - c0;
+  }
 }
 
 }  // namespace
@@ -69,11 +101,16 @@ int moe_ceiling_read(const void* buf, size_t bytes, uint32_t* sink, void* stream
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-int moe_ceiling_mfma(int32_t iters, float* sink, double* flops, void* stream) {
+// iters loop trips of 4 kMfmaChains operations per wave; clocks (optional)
+// receives 2 values per block (kMfmaBlocks blocks): real-time and shader-clock
+// ticks over the loop.
+int moe_ceiling_mfma(int32_t iters, int32_t random, float* sink, unsigned long long* clocks,
+                     double* flops, void* stream) {
   if (iters <= 0 || !sink || !flops) return -1;
-  *flops = (double)moe::kMfmaBlocks * (moe::kCeilThreads / 64) * moe::kMfmaChains * iters * (16.0 * 16 * 32 * 2);
+  *flops = (double)moe::kMfmaBlocks * (moe::kCeilThreads / 64) * moe::kMfmaChains * 4.0 * iters *
+           (16.0 * 16 * 32 * 2);
   hipLaunchKernelGGL(moe::ceiling_mfma_kernel, dim3(moe::kMfmaBlocks), dim3(moe::kCeilThreads), 0,
-                     (hipStream_t)stream, (int)iters, sink);
+                     (hipStream_t)stream, (int)iters, (int)random, sink, clocks);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

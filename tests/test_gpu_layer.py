@@ -603,10 +603,15 @@ def test_ceiling_helpers_run():
     import torch
     buf = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(2 * B.CEILING_MFMA_BLOCKS, dtype=torch.int64, device="cuda")
     B.moe_ceiling_read(buf, sink)
-    flops = B.moe_ceiling_mfma(8, sink)
-    torch.cuda.synchronize()
-    assert flops == 1024 * 4 * 8 * 8 * (16 * 16 * 32 * 2)
+    for random in (True, False):
+        flops = B.moe_ceiling_mfma(8, sink, random=random, clocks=clocks)
+        torch.cuda.synchronize()
+        assert flops == 1024 * 4 * 8 * 4 * 8 * (16 * 16 * 32 * 2)
+        mhz = B.ceiling_clock_mhz(clocks)
+        print(f"matrix-core loop, random operands {random}: shader clock {mhz:.0f} MHz", flush=True)
+        assert 100.0 < mhz < 4000.0
     assert torch.count_nonzero(sink).item() == 0
     with pytest.raises(B.MoeError):
         B.moe_ceiling_read(buf[:15], sink)  # not a multiple of 16 bytes
