@@ -1,11 +1,11 @@
 """GPU layer parity against the CPU oracle, through the C ABI.
 
 Covers every workload shape: the tiny layer (all tokens, ragged token counts),
-the 512-token prefill (all tokens), the Zipf-skewed 2048-token prefill
-(sampled tokens incl. the heaviest experts' tokens, routing metadata), the
-16384-token prompt in 4096-token chunks (sampled tokens; chunked equals
-unchunked bit for bit), decode at 1 and 4 tokens, plus edge cases (forced
-heavy routing with empty experts, determinism, T = 0).
+the 512-token prefill (all tokens), the Zipf-skewed 2048-token prefill (all
+tokens, routing metadata), the 16384-token prompt in 4096-token chunks (all
+tokens; chunked equals unchunked bit for bit), decode at 1 and 4 tokens, a
+seeded sweep of token counts, chunk sizes and GEMM choices (all tokens), plus
+edge cases (forced heavy routing with empty experts, determinism, T = 0).
 """
 import numpy as np
 import pytest
@@ -173,6 +173,31 @@ def test_prefill_skew_t2048_all_tokens(torch_cuda):
     assert np.array_equal(logits, logits2)
     s2 = check_layer(x, w, y2, logits2, idx, wsel)
     print(f"skew T=2048 in 512-token chunks: {s2}", flush=True)
+
+
+# Seeded sweep: token counts from 1 to 2600, chunked or not (chunk sizes that
+# leave ragged last chunks), each GEMM choice, on the near-uniform and the
+# Zipf-skewed layer. Every token against the oracle, with the selections
+# re-derived for all tokens from the GPU's logits (the route output holds the
+# last chunk only).
+@pytest.mark.parametrize("case", range(8))
+def test_prefill_random_shapes_all_tokens(torch_cuda, case):
+    rng = np.random.default_rng(7000 + case)
+    name = ("prefill_t512", "skew_t2048")[case % 2]
+    gemm = (B.GEMM_AUTO, B.GEMM_EXACT, B.GEMM_WIDE, B.GEMM_AUTO)[case % 4]
+    wl, w, dw = _layer(name)
+    T = int(rng.integers(1, 2601))
+    chunk = int(rng.choice([0, 0, 96, 517, 1024]))
+    x = synth.make_x(rng, T, w.H)
+    d = B.dims(w.H, w.I, w.E, gemm=gemm)
+    print(f"case {case}: {name} T={T} chunk={chunk} gemm={gemm}", flush=True)
+    y, logits, _ = _prefill(torch_cuda, dw, x, chunk=chunk, route=False, d=d)
+    ro = B.RouteBuffers(d, T)
+    B.moe_route(d, torch_cuda.from_numpy(logits).cuda(), T, ro, B.workspace(d, T, B.MODE_ROUTE))
+    torch_cuda.cuda.synchronize()
+    idx, wsel = _route_of(ro.to_numpy(), T)
+    s = check_layer(x, w, y, logits, idx, wsel)
+    print(f"case {case}: {s}", flush=True)
 
 
 def test_prefill_long_chunked_all_tokens(torch_cuda):
