@@ -290,14 +290,21 @@ int moe_test_dequant(const void* blob, int32_t count, int32_t N, int32_t K, int3
  * HBM bandwidth use a buffer much larger than the 256 MB last-level cache.
  *
  * moe_ceiling_mfma enqueues 1024 blocks of four waves, each wave running
- * eight independent chains of `iters` 16x16x32 bf16 matrix-core operations
- * on register operands, and stores the flop count of the launch in *flops
- * (host). `sink` as above.
+ * eight independent chains of 4 * `iters` (iters > 0) 16x16x32 bf16
+ * matrix-core operations on register operands, and stores the flop count of
+ * the launch in *flops (host). `random` nonzero: the operands are random bf16
+ * values (magnitude in [0.5, 1), random sign) that change from one operation
+ * to the next, as layer data does; zero: nearly constant operands. The
+ * device sustains a lower clock on the first. `clocks` (device, may be null):
+ * 2048 unsigned 64-bit values that receive, per block, the real-time ticks
+ * (100 MHz) and the shader-clock ticks over its loop; their sums give the
+ * clock the launch ran at. `sink` as above.
  *
  * Both return MOE_EINVAL for null pointers or bad sizes, MOE_EHIP if the
  * launch fails; they allocate nothing and do not synchronise. */
 int moe_ceiling_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
-int moe_ceiling_mfma(int32_t iters, float* sink, double* flops, void* stream);
+int moe_ceiling_mfma(int32_t iters, int32_t random, float* sink, unsigned long long* clocks,
+                     double* flops, void* stream);
 
 #ifdef __cplusplus
 }

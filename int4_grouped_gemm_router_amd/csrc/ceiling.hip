@@ -3,6 +3,7 @@
 // operations. They are not part of the layer: they give the achievable HBM
 // read bandwidth and bf16 MFMA rate, so that roofline fractions can be stated
 // against measured ceilings as well as against the published peaks.
+#include "../../include/moe_int4.h"
 #include "device.h"
 
 namespace moe {
@@ -95,10 +96,10 @@ __global__ __launch_bounds__(kCeilThreads) void ceiling_mfma_kernel(int iters, i
 extern "C" {
 
 int moe_ceiling_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
-  if (!buf || !sink || bytes < 16 || bytes % 16) return -1;
+  if (!buf || !sink || bytes < 16 || bytes % 16) return MOE_EINVAL;
   hipLaunchKernelGGL(moe::ceiling_read_kernel, dim3(moe::kReadBlocks), dim3(moe::kCeilThreads), 0,
                      (hipStream_t)stream, static_cast<const moe::u32x4*>(buf), (int64_t)(bytes / 16), sink);
-  return hipGetLastError() == hipSuccess ? 0 : -4;
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 // iters loop trips of 4 kMfmaChains operations per wave; clocks (optional)
@@ -106,12 +107,12 @@ int moe_ceiling_read(const void* buf, size_t bytes, uint32_t* sink, void* stream
 // ticks over the loop.
 int moe_ceiling_mfma(int32_t iters, int32_t random, float* sink, unsigned long long* clocks,
                      double* flops, void* stream) {
-  if (iters <= 0 || !sink || !flops) return -1;
+  if (iters <= 0 || !sink || !flops) return MOE_EINVAL;
   *flops = (double)moe::kMfmaBlocks * (moe::kCeilThreads / 64) * moe::kMfmaChains * 4.0 * iters *
            (16.0 * 16 * 32 * 2);
   hipLaunchKernelGGL(moe::ceiling_mfma_kernel, dim3(moe::kMfmaBlocks), dim3(moe::kCeilThreads), 0,
                      (hipStream_t)stream, (int)iters, (int)random, sink, clocks);
-  return hipGetLastError() == hipSuccess ? 0 : -4;
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 }  // extern "C"
