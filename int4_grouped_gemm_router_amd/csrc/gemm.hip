@@ -12,8 +12,9 @@
 // persistent: every block streams its units back to back and starts loading
 // the next unit while the current one finishes, so the memory pipeline does
 // not drain between units. Two kernels share the per-group arithmetic:
-//   gemm_ring_kernel    K a multiple of 256 (the main path): register ring of
-//                       plain loads, three groups ahead, see below;
+//   gemm_ring_kernel    K a multiple of 128 (the main path, every supported
+//                       shape): register ring of plain loads, one group
+//                       ahead, see below;
 //   gemm_stream_kernel  any other K: an LDS ring filled by asynchronous
 //                       global -> LDS copies with explicit vmcnt waits.
 //
@@ -357,23 +358,25 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs a) {
 
 // ------------------------------------------------------------------ register-ring kernel
 //
-// The main path for K a multiple of 256 (G % 4 == 0). Three blocks of four
+// The main path for K a multiple of 128 (G % 2 == 0). Three blocks of four
 // waves per compute unit (three waves per SIMD, so one wave's waits are
 // covered by the others); each wave owns 64 columns. Every load of the loop
 // is a plain register load: per wave and group the packed codes (2 KB), a
 // 1 KB share of the gathered activation rows and a 256-byte share of the
-// scale/bias words are loaded into a four-deep register ring three groups
-// ahead (about 120 KB per compute unit in flight). At its turn a group's
-// activation and scale/bias shares are written to a two-stage LDS buffer, one
-// barrier, and all four waves read them. Unit boundaries fall on multiples of
-// four groups, so every ring slot index is static and the loads for the next
+// scale/bias words are loaded into a two-deep register ring one group ahead
+// (about 40 KB per compute unit in flight, some 10 MB on the chip: what HBM
+// needs at its loaded latency; three groups ahead, 30 MB in flight, made the
+// 512-token gate/up 5% and down 3% slower). At its turn a group's activation
+// and scale/bias shares are written to a two-stage LDS buffer, one barrier,
+// and all four waves read them. Unit boundaries fall on multiples of two
+// groups, so every ring slot index is static and the loads for the next
 // unit start while the current one finishes. Loads of one kind complete in
-// order, so the compiler's own wait counts keep three groups in flight (no
+// order, so the compiler's own wait counts keep a group in flight (no
 // asynchronous LDS copies are mixed in, which would force full drains).
 
 constexpr int kRWaves = 4;
 constexpr int kRThreads = kRWaves * 64;
-constexpr int kRS = 4;         // ring depth in groups (K / 64 must be a multiple)
+constexpr int kRS = 2;         // ring depth in groups (K / 64 must be a multiple)
 constexpr int kRBlocksPerCU = 3;
 
 struct RingLds {
