@@ -11,12 +11,8 @@
 // column tile of the output; each wave owns 64 columns. The grid is
 // persistent: every block streams its units back to back and starts loading
 // the next unit while the current one finishes, so the memory pipeline does
-// not drain between units. Two kernels share the per-group arithmetic:
-//   gemm_ring_kernel    K a multiple of 128 (the main path, every supported
-//                       shape): register ring of plain loads, one group
-//                       ahead, see below;
-//   gemm_stream_kernel  any other K: an LDS ring filled by asynchronous
-//                       global -> LDS copies with explicit vmcnt waits.
+// not drain between units (gemm_ring_kernel: a register ring of plain loads,
+// one group ahead, see below; K a multiple of 128).
 //
 // Per group and 16x16 output tile, with the codes expanded to the exact bf16
 // values 128 + q by two bit operations:
@@ -36,40 +32,8 @@
 
 namespace moe {
 
-constexpr int kWaves = 8;                        // waves per block, 64 columns each
-constexpr int kThreads = kWaves * 64;
 constexpr int kBatch = 16;                       // units whose row tables a block stages at once
 constexpr int kXBytes = kItemRows * kGroup * 2;  // gathered activations per group: 4 KB
-constexpr int kCopiesPerStep = 4;                // copies per wave per group: x, 2 x codes, scale/bias
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Asynchronous global -> LDS copies; lane l writes dst + size * l.
-__device__ inline void dma16(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
-}
-
-// Wait until at most n (a multiple of four, <= 24) of this wave's vector
-// memory operations are pending. Asynchronous copies complete in issue order
-// among themselves, so this guarantees every copy issued before the last n
-// copies has landed.
-__device__ inline void wait_vm(int n) {
-  if (n >= 24)
-    asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-  else if (n >= 20)
-    asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
-  else if (n >= 16)
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (n >= 12)
-    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  else if (n >= 8)
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if (n >= 4)
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
 // Keeps the compiler from moving LDS accesses across this point (the
 // epilogue transposes through LDS with differently typed accesses).
 __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
@@ -79,17 +43,6 @@ struct UnitInfo {
   int row0;    // first row (sorted pair position, or k*T + first token for the shared expert)
   int rows;    // 1..item_rows
   int nt;      // column tile
-};
-
-template <int S>
-struct GemmLds {
-  u32x4 x[S][kXBytes / 16];             // [stage][ms 2][c 8][row 16]
-  u32x4 code[S][kWaves][2][64];         // [stage][wave][half][lane]
-  u32x4 sb[S][kWaves][16];              // [stage][wave][c16]: 4 scales, 4 biases
-  UnitInfo unit[kBatch];
-  int rowidx[kBatch][kItemRows];        // activation row of each item row
-  int outrow[kBatch][kItemRows];        // down: pair p (routed) or token t (shared)
-  u32x4 tr[kWaves][64];                 // per-wave epilogue transpose (1 KB)
 };
 
 // Down output of one row and four consecutive columns: a routed row (pair p)
@@ -157,201 +110,6 @@ __device__ __forceinline__ void ring_step_bf16(const u32x4 (&w)[8], const u32x4*
     for (int ct = 0; ct < 4; ++ct) {
       acc[ms][ct] = mfma16(a0, w[2 * ct], acc[ms][ct]);
       acc[ms][ct] = mfma16(a1, w[2 * ct + 1], acc[ms][ct]);
-    }
-  }
-}
-
-// ------------------------------------------------------------------ LDS-stream kernel
-//
-// The general path (any K that is a multiple of 128). One block of eight
-// waves per compute unit, 512 columns per unit. Per group the activation rows
-// (4 KB), each wave's codes (2 KB) and scale/bias words (256 B) arrive in an
-// S-stage LDS ring by asynchronous global -> LDS copies, S - 1 groups ahead
-// and across unit boundaries; no global load of the loop targets registers.
-template <int MODE, int S>
-__global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs a) {
-  __shared__ GemmLds<S> L;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c16 = lane & 15, kb = lane >> 4;
-  const int K = a.K, G = K / kGroup;
-  const PackGeom geom = pack_geom(a.N, K, a.paired);
-  const int n_wt = geom.n_wt;
-  const int n_tiles = (n_wt + kWaves - 1) / kWaves;
-
-  // Blocks are dispatched round-robin over the 8 XCDs (block b on XCD b & 7).
-  const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, nbx = gridDim.x >> 3;
-  const int ni = *a.num_items;
-  const int n_slots = ni + a.shared_slots;
-  // XCD x owns the contiguous unit range [u0, u1) (units are slot-major), so
-  // the column tiles of one item, and the items of one expert, share an L2
-  const int n_units = n_slots * n_tiles;
-  const int u0 = (int)((int64_t)n_units * xcd / 8), u1 = (int)((int64_t)n_units * (xcd + 1) / 8);
-  const int my_units = u1 - u0 > lb ? (u1 - u0 - lb + nbx - 1) / nbx : 0;
-  const ExpandConsts xk = expand_consts();
-
-  // lane roles in the copies
-  const int xu = 32 * wave + (lane & 31);                         // 16-byte unit of the x stage
-  const int xm = (xu >> 7) * 16 + (xu & 15), xc = (xu >> 4) & 7;  // its row and chunk
-
-  for (int base = 0; base < my_units; base += kBatch) {
-    const int nb = min(kBatch, my_units - base);
-    lds_barrier();  // the previous batch is done with the tables
-    if (tid < nb) {
-      const int v = u0 + lb + (base + tid) * nbx;
-      const int slot = v / n_tiles;
-      UnitInfo u;
-      u.nt = v % n_tiles;
-      if (slot < ni) {
-        u.expert = a.items[3 * slot];
-        u.row0 = a.items[3 * slot + 1];
-        u.rows = a.items[3 * slot + 2];
-      } else {
-        const int t0 = (slot - ni) * a.item_rows;
-        u.expert = -1;
-        u.row0 = a.k * a.T + t0;
-        u.rows = min(a.item_rows, a.T - t0);
-      }
-      L.unit[tid] = u;
-    }
-    lds_barrier();
-    for (int e = tid; e < nb * kItemRows; e += kThreads) {
-      const int j = e / kItemRows, m = e % kItemRows;
-      const UnitInfo u = L.unit[j];
-      const int mm = m < u.rows ? m : 0;  // rows past the item copy row 0 (never stored)
-      if (MODE == kGateUp) {
-        L.rowidx[j][m] = u.expert >= 0 ? a.perm[u.row0 + mm] / a.k : u.row0 - a.k * a.T + mm;
-      } else {
-        L.rowidx[j][m] = u.row0 + mm;
-        int orow;
-        if (u.expert >= 0) {
-          const int p = a.perm[u.row0 + mm];
-          orow = p;  // routed output row of pair p = t*k + j
-        } else {
-          orow = u.row0 - a.k * a.T + mm;  // shared output row: the token
-        }
-        L.outrow[j][m] = orow;
-      }
-    }
-    lds_barrier();
-
-    // ---- copy side: unit iu, group ig
-    const int total = nb * G;
-    int iu = 0, ig = 0;
-    const uint16_t* xsrc = nullptr;
-    const uint8_t* nsrc = nullptr;
-    const uint8_t* bsrc = nullptr;
-    auto set_copy_unit = [&](int j) {
-      const int expert = __builtin_amdgcn_readfirstlane(L.unit[j].expert);
-      const int nt = __builtin_amdgcn_readfirstlane(L.unit[j].nt);
-      const int wt = min(nt * kWaves + wave, n_wt - 1);  // idle waves copy a valid tile
-      const uint8_t* eb = expert >= 0 ? a.blob + (int64_t)expert * a.expert_bytes : a.shared_blob;
-      nsrc = eb + geom.nib_off + (int64_t)wt * G * kNibBytes + lane * 16;
-      bsrc = eb + geom.sb_off + (int64_t)wt * G * kSbBytes + (lane & 15) * 16;
-      xsrc = a.act + (int64_t)L.rowidx[j][xm] * K + 8 * xc;
-    };
-    auto issue = [&](int st) {
-      if (lane < 32) dma16(xsrc + ig * kGroup, &L.x[st][32 * wave]);
-      dma16(nsrc + (int64_t)ig * kNibBytes, &L.code[st][wave][0][0]);
-      dma16(nsrc + (int64_t)ig * kNibBytes + 1024, &L.code[st][wave][1][0]);
-      if (lane < 16) dma16(bsrc + (int64_t)ig * kSbBytes, &L.sb[st][wave][0]);
-      if (++ig == G) {
-        ig = 0;
-        if (++iu < nb) set_copy_unit(iu);
-      }
-    };
-    set_copy_unit(0);
-    for (int d = 0; d < S - 1; ++d)
-      if (d < total) issue(d);
-
-    // ---- compute side: unit cu, group cg, stage st
-    f32x4 acc[2][4];
-    int cu = 0, cg = 0, st = 0;
-    int rows = 0, nsub = 0, nt = 0, row0 = 0;
-    bool routed = true;
-    bool active = false;
-    for (int s = 0; s < total; ++s) {
-      wait_vm(kCopiesPerStep * min(S - 2, total - 1 - s));
-      // all waves' copies of this group have landed, and every wave is done
-      // with the stage the next copies overwrite
-      lds_barrier();
-      if (s + S - 1 < total) issue(st == 0 ? S - 1 : st - 1);
-      if (cg == 0) {
-        rows = __builtin_amdgcn_readfirstlane(L.unit[cu].rows);
-        routed = __builtin_amdgcn_readfirstlane(L.unit[cu].expert) >= 0;
-        row0 = __builtin_amdgcn_readfirstlane(L.unit[cu].row0);
-        nt = __builtin_amdgcn_readfirstlane(L.unit[cu].nt);
-        nsub = (rows + 15) >> 4;
-        active = nt * kWaves + wave < n_wt;
-#pragma unroll
-        for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct) acc[ms][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      if (active) {
-        const u32x4 w0 = L.code[st][wave][0][lane];
-        const u32x4 w1 = L.code[st][wave][1][lane];
-        const u32x4 sbv = L.sb[st][wave][c16];
-        const u32x4* xst = &L.x[st][0];
-        if (nsub == 2)
-          ring_step<2>(w0, w1, sbv, xst, kb, c16, xk, acc);
-        else
-          ring_step<1>(w0, w1, sbv, xst, kb, c16, xk, acc);
-      }
-
-      if (cg == G - 1) {
-        const int wt = nt * kWaves + wave;
-        if (MODE == kGateUp) {
-          const int I = a.N;
-          if (active) {
-            uint16_t* trb = reinterpret_cast<uint16_t*>(&L.tr[wave][0]);
-            const int rr = lane >> 2, ch = lane & 3;
-#pragma unroll
-            for (int ms = 0; ms < 2; ++ms) {
-              if (ms < nsub) {
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                  for (int i = 0; i < 4; ++i)
-                    trb[(4 * kb + i) * 32 + 16 * ct + c16] =
-                        f2bf(silu(acc[ms][2 * ct][i]) * acc[ms][2 * ct + 1][i]);
-                compiler_fence();
-                const u32x4 v = L.tr[wave][rr * 4 + ch];  // row rr of the 16 x 32 tile
-                compiler_fence();
-                if (16 * ms + rr < rows)
-                  *reinterpret_cast<u32x4*>(a.h_out + (int64_t)(row0 + 16 * ms + rr) * I + 32 * wt +
-                                            8 * ch) = v;
-              }
-            }
-          }
-        } else {
-          if (active) {
-            float* trf = reinterpret_cast<float*>(&L.tr[wave][0]);
-            const int rr = lane >> 2, c4 = lane & 3;
-#pragma unroll
-            for (int ms = 0; ms < 2; ++ms) {
-              if (ms < nsub) {
-                const int r = 16 * ms + rr;
-                const int orow = L.outrow[cu][r < rows ? r : 0];
-#pragma unroll
-                for (int ct = 0; ct < 4; ++ct) {
-#pragma unroll
-                  for (int i = 0; i < 4; ++i) trf[(4 * kb + i) * 16 + c16] = acc[ms][ct][i];
-                  compiler_fence();
-                  const f32x4 v = *reinterpret_cast<const f32x4*>(&trf[rr * 16 + 4 * c4]);
-                  compiler_fence();
-                  if (r < rows) store_down(a, routed, orow, 64 * wt + 16 * ct + 4 * c4, v);
-                }
-              }
-            }
-          }
-        }
-      }
-      if (++cg == G) {
-        cg = 0;
-        ++cu;
-      }
-      if (++st == S) st = 0;
     }
   }
 }
@@ -743,15 +501,11 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s, int grid_blocks) {
   }
   const int G = a.K / kGroup;
   if (G < 2 || G > kMaxGroups) return hipErrorInvalidValue;
-  const int cus = compute_units();
+  // every supported shape has an even group count (H % 256 == 0, I % 128 == 0)
+  if (G % kRS) return hipErrorInvalidValue;
   const int exact = (grid_blocks + 7) / 8 * 8;
-  if (G % kRS == 0) {
-    const dim3 grid(grid_blocks > 0 ? exact : kRBlocksPerCU * cus), block(kRThreads);
-    hipLaunchKernelGGL((gemm_ring_kernel<MODE, false>), grid, block, 0, s, a);
-    return hipGetLastError();
-  }
-  const dim3 grid(grid_blocks > 0 ? exact : cus), block(kThreads);
-  hipLaunchKernelGGL((gemm_stream_kernel<MODE, 6>), grid, block, 0, s, a);
+  const dim3 grid(grid_blocks > 0 ? exact : kRBlocksPerCU * compute_units()), block(kRThreads);
+  hipLaunchKernelGGL((gemm_ring_kernel<MODE, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

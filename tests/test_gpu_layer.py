@@ -429,7 +429,7 @@ def test_decode_tiny_and_vs_prefill(torch_cuda):
 
 # Other sizes of the same layer family, chosen to reach the paths the main
 # shapes do not: (1024, 384, E=128): gate/up over 16 groups, down over K = 384
-# (6 groups, the LDS-stream GEMM); (4096, 256, E=64): gate/up over 64 groups
+# (6 groups: not a multiple of four); (4096, 256, E=64): gate/up over 64 groups
 # (the most the GEMMs and the decode kernels take), down over 4 groups;
 # (768, 640, E=192): 12 and 10 groups; (256, 4096, E=64): the largest
 # intermediate size, down over 64 groups (eight rounds in the decode down
@@ -642,14 +642,14 @@ def test_ceiling_helpers_run():
         B.moe_ceiling_read(buf[:15], sink)  # not a multiple of 16 bytes
 
 
-# The exact 32-row GEMMs at family sizes whose down projection takes the
-# LDS-stream kernel (I / 64 not a multiple of 4: I = 384 and 640), on 8192
-# tokens: about 20 work units per persistent block, so the hand-off of copies
+# The exact 32-row GEMMs at family sizes whose down projection has a group
+# count that is not a multiple of four (I / 64 = 6 and 10), on 8192 tokens:
+# about 20 work units per persistent block, so the ring's hand-off of loads
 # to the next unit and the rollover past a block's 16-unit batch both run.
 # Every token against the oracle; the wide kernels on the same inputs too
 # (their half-filled last column tile at I = 384 and 640).
 @pytest.mark.parametrize("H,I,E", [(1024, 384, 128), (768, 640, 192)])
-def test_exact_stream_kernel_long_run(torch_cuda, H, I, E):
+def test_exact_gemm_long_run_odd_group_pairs(torch_cuda, H, I, E):
     rng = np.random.default_rng(H * 7 + I)
     w = synth.make_weights(rng, H, I, E)
     dw = B.DeviceWeights.from_logical(w)
