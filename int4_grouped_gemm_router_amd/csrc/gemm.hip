@@ -34,7 +34,6 @@ namespace moe {
 
 constexpr int kBatch = 16;                       // units whose row tables a block stages at once
 constexpr int kXBytes = kItemRows * kGroup * 2;  // gathered activations per group: 4 KB
-
 // Keeps the compiler from moving LDS accesses across this point (the
 // epilogue transposes through LDS with differently typed accesses).
 __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
