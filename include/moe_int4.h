@@ -73,8 +73,8 @@ extern "C" {
  *                   (fp32 value rounded once to bf16) and the matrix cores
  *                   accumulate x.w in fp32; suited to long chunks, where many
  *                   rows share each expanded weight;
- *   MOE_GEMM_AUTO   (0) WIDE for chunks whose pairs average at least 32 rows
- *                   per expert (top_k * T_chunk >= 32 * E), else EXACT.
+ *   MOE_GEMM_AUTO   (0) WIDE for chunks whose pairs average at least 36 rows
+ *                   per expert (top_k * T_chunk >= 36 * E), else EXACT.
  * (diariobitcoin.com, "Perplexity libera Lily...", section "Las
  * optimizaciones en el prefill": the grouped GEMM reconstructs the 4-bit
  * weights block by block on chip with fp32 accumulation.) Decode ignores

@@ -22,7 +22,7 @@ bool dims_ok(const moe_dims* d) {
 // then enough rows share each expanded weight for the matrix cores to set
 // the pace; below it the layer streams weights and the exact kernels' short
 // items spread them over more compute units.
-constexpr int kWideMinRows = 32;
+constexpr int kWideMinRows = 36;  // the measured crossover lies between 32 and 36 (E = 256)
 bool use_wide(const moe_dims* d, int Tn) {
   if (d->gemm == MOE_GEMM_EXACT) return false;
   if (d->gemm == MOE_GEMM_WIDE) return true;

@@ -474,15 +474,15 @@ def test_other_family_sizes_wide(torch_cuda, H, I, E):
 
 
 def test_gemm_auto_threshold(torch_cuda):
-    # the automatic choice takes the wide GEMMs from 32 pairs per expert on
-    # (8 T >= 32 E: T >= 1024 at E = 256): bit for bit the forced choice on
+    # the automatic choice takes the wide GEMMs from 36 pairs per expert on
+    # (8 T >= 36 E: T >= 1152 at E = 256): bit for bit the forced choice on
     # each side of the threshold, and the two choices differ
     _, w, dw = _layer("prefill_t512")
-    x = synth.make_x(np.random.default_rng(33), 1024, w.H)
+    x = synth.make_x(np.random.default_rng(33), 1152, w.H)
     auto = B.dims(w.H, w.I)
     exact = B.dims(w.H, w.I, gemm=B.GEMM_EXACT)
     wide = B.dims(w.H, w.I, gemm=B.GEMM_WIDE)
-    for T, same in ((1023, exact), (1024, wide)):
+    for T, same in ((1151, exact), (1152, wide)):
         ya, _, _ = _prefill(torch_cuda, dw, x[:T], route=False, d=auto)
         yf, _, _ = _prefill(torch_cuda, dw, x[:T], route=False, d=same)
         other = wide if same is exact else exact
