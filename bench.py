@@ -379,6 +379,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--block-m", type=int, default=32, choices=(16, 32),
                     help="routing block size = GEMM work-item rows (ablation; 32 by default)")
+    ap.add_argument("--gemm", default="auto", choices=("auto", "exact", "wide"),
+                    help="grouped GEMM design (ablations; the automatic choice by default)")
     ap.add_argument("--unfused", action="store_true",
                     help="ablation: time moe_prefill_layer_unfused against the fused call")
     ap.add_argument("--host-routing", action="store_true",
@@ -403,7 +405,8 @@ def main():
         from int4_grouped_gemm_router_amd import binding as B
         rows = []
         for name in ("prefill_t512", "skew_t2048"):
-            r, _ = run_prefill(name, args.steps, args.warmup, args.copies)
+            r, _ = run_prefill(name, args.steps, args.warmup, args.copies,
+                               gemm={"auto": 0, "exact": 1, "wide": 2}[args.gemm])
             wl, w, x, xd, dws = prefill_setup(name, args.copies)
             d = dws[0].dims
             T = wl.T
@@ -431,7 +434,8 @@ def main():
         from int4_grouped_gemm_router_amd import binding as B
         rows = []
         for name in ("prefill_t512", "skew_t2048"):
-            r, _ = run_prefill(name, args.steps, args.warmup, args.copies)
+            r, _ = run_prefill(name, args.steps, args.warmup, args.copies,
+                               gemm={"auto": 0, "exact": 1, "wide": 2}[args.gemm])
             wl, w, x, xd, dws = prefill_setup(name, args.copies)
             d = dws[0].dims
             T = wl.T
@@ -478,8 +482,9 @@ def main():
                           "dtype": "bf16", "data": "synthetic",
                           "config": {"workload": args.workload, "T": r["T"]}, "decode": r}), flush=True)
         return
+    gemm = {"auto": 0, "exact": 1, "wide": 2}[args.gemm]
     res, (w, x) = run_prefill(args.workload, args.steps, args.warmup, args.copies,
-                              block_m=args.block_m)
+                              block_m=args.block_m, gemm=gemm)
     log(f"{args.workload}: {res}")
     gu_us = res["kernels_us"]["gemm_gateup"]
     dominant = max(res["kernels_us"], key=res["kernels_us"].get)
@@ -511,7 +516,7 @@ def main():
                    "top_k": 8, "shared_experts": 1,
                    "weights": "int4 affine, groups of 64, bf16 scale+bias",
                    "weight_copies": args.copies, "launch": "hip graph per layer call",
-                   "block_m": args.block_m,
+                   "block_m": args.block_m, "gemm": args.gemm,
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "ceilings": ceil,
